@@ -1,0 +1,205 @@
+"""fp64 CPU oracle of CCA attention: visibility, global-aware pooling, fused softmax.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing in the product
+path imports this module.
+
+What it computes, in the pages' order:
+
+1. Grouping.  Tokens 0..L-1 are cut into non-overlapping groups of ``g``
+   consecutive tokens, group ``i`` holding tokens ig..ig+g-1 ([article],
+   global-aware pooling paragraph: the sequence is split into non-overlapping
+   groups; [digest], Method, pooling formula: index set I_i).  Only complete
+   groups exist, m = floor(L/g) of them.
+
+2. Global-aware pooling ([digest], Method, pooling formula; [article]: the
+   importance scores come from the query of the group's *last* token against
+   all keys of the group; [card], Approach).  For group i:
+       s_tau = q_last . K[ig+tau] / sqrt(d),   a = softmax(s),
+       core key   CK_i = sum_tau a_tau K[ig+tau],
+       core value CV_i = sum_tau a_tau V[ig+tau].
+   The pages pool the token representations X and then apply the key/value
+   projections, which are shared with the local module ([article]: the two
+   modules share the linear transformation parameters).  Because the weights
+   sum to one, pooling X and then projecting equals pooling the projected keys
+   and values, for any affine projection; the oracle pools the given
+   (already projected) K and V.
+
+3. Fusion ([digest], Method, fusion formula; [card], Approach: one softmax over
+   both; [article]: the local module guarantees every token attends to at least
+   the previous w raw tokens).  Query t attends, with ONE softmax, to the
+   concatenation [visible core tokens ; raw keys of the local window]:
+       o_t = softmax(q_t [CK_T ; K_U]^T / sqrt(d)) [CV_T ; V_U].
+
+Readings of what the pages leave open (each is a choice, stated once here):
+  R-1  Groups start at token 0; a trailing partial group (L mod g != 0) has no
+       core token; its tokens are reached only through the window.
+  R-2  Visibility sets (the fusion formula names them but never defines them):
+       U_t = raw positions max(0, t-w+1) .. t (w tokens including t itself);
+       T_t = cores j whose last token (j+1)g-1 < t-w+1, i.e. groups lying
+       wholly before the window.  Hence n_core(t) = max(0, floor((t-w+1)/g)).
+       Up to g-1 tokens between the last visible core and the window are seen
+       by neither module; nothing is seen twice.
+  R-3  "Last token of group i" is 0-indexed row (i+1)g-1.
+  R-4  d is the head dimension; both softmaxes scale by 1/sqrt(d).
+  R-5  K and V are pooled after projection and rotation (they arrive that way).
+  R-7  g >= 1 and w >= 1; the visible set always holds t itself.
+  R-8  GQA (the rebuttal, answer on GQA, says pooling "may need adjusting";
+       no rule is given): one core pair per (kv head, group); the pooling
+       query is the mean of the group's last-token queries over the G query
+       heads that share the kv head.  PARITY UNPINNED by the pages: pinned
+       only by the G = 1 reduction and by "G identical heads == one head".
+  R-9  Query head h reads kv head floor(h / G).
+  R-10 Decode row t is prefill row t of the sequence extended to t+1 tokens;
+       the core of a group that completes at t is pooled with q_t and is not
+       visible to t itself.
+
+Arithmetic: every value is widened to float64 (bf16 and fp32 widen exactly)
+and nothing is rounded back.  Each output row is computed on its own from its
+own index sets; numpy matrix-vector products and reductions are the only
+library primitives.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ---------------------------------------------------------------- visibility
+
+
+def win_lo(t: int, w: int) -> int:
+    """First raw position of the local window of query t (reading R-2)."""
+    return max(0, t - w + 1)
+
+
+def n_core(t: int, g: int, w: int) -> int:
+    """Number of cores visible to query t: groups wholly before the window (R-2)."""
+    return max(0, (t - w + 1) // g) if t - w + 1 > 0 else 0
+
+
+def group_last(j: int, g: int) -> int:
+    """Index of the last token of group j, whose query scores the group (R-3)."""
+    return (j + 1) * g - 1
+
+
+def visibility(L: int, g: int, w: int):
+    """Integer tables: n_core[L], win_lo[L], group_last[floor(L/g)] (int64)."""
+    t = np.arange(L, dtype=np.int64)
+    lo = np.maximum(0, t - w + 1)
+    nc = np.where(t - w + 1 > 0, (t - w + 1) // g, 0)
+    gl = (np.arange(L // g, dtype=np.int64) + 1) * g - 1
+    return nc, lo, gl
+
+
+def visible_pairs_total(L: int, g: int, w: int) -> int:
+    """Sum over queries t < L of the number of visible keys (cores + window)."""
+    nc, lo, _ = visibility(L, g, w)
+    return int(nc.sum() + (np.arange(L) - lo + 1).sum())
+
+
+def cache_tokens(L: int, g: int, w: int) -> int:
+    """Tokens a decoder must keep after L tokens: every complete core plus the
+    last w raw tokens ([rebuttal], answer on 128K contexts, gives the KV cache
+    of LLaMA2-7B at 128K as 4.5 GB against 64 GB for full attention)."""
+    return L // g + min(w, L)
+
+
+# ----------------------------------------------------------------- helpers
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
+    """Max-subtracted softmax along ``axis`` (masked entries are -inf)."""
+    m = np.max(s, axis=axis, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+# ------------------------------------------------------------------- pooling
+
+
+def pool_core(Q, K, V, g: int):
+    """Global-aware pooling ([digest], Method, pooling formula).
+
+    Q [B,Hq,L,d]; K, V [B,Hkv,L,d] (any float dtype; widened to fp64).
+    Returns CK, CV [B,Hkv,m,d] and the pooling weights A [B,Hkv,m,g], m = L//g.
+    """
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    m = L // g
+    if m == 0:
+        z = np.zeros((B, Hkv, 0, d))
+        return z, z.copy(), np.zeros((B, Hkv, 0, g))
+    last = np.array([group_last(j, g) for j in range(m)])
+    # query of each group's last token, one per query head: [B,Hq,m,d]
+    q_last = _f64(Q[:, :, last, :])
+    # R-8: one pooling query per kv head = mean over its G query heads
+    q_bar = q_last.reshape(B, Hkv, G, m, d).mean(axis=2)
+    Kg = _f64(K[:, :, : m * g, :]).reshape(B, Hkv, m, g, d)
+    Vg = _f64(V[:, :, : m * g, :]).reshape(B, Hkv, m, g, d)
+    s = np.einsum("bhmd,bhmtd->bhmt", q_bar, Kg) / math.sqrt(d)
+    A = _softmax(s, axis=-1)
+    CK = np.einsum("bhmt,bhmtd->bhmd", A, Kg)
+    CV = np.einsum("bhmt,bhmtd->bhmd", A, Vg)
+    return CK, CV, A
+
+
+# ------------------------------------------------------------------- fusion
+
+
+def attn_rows(Q, K, V, CK, CV, g: int, w: int, ts):
+    """Fused attention rows ([digest], Method, fusion formula) for positions ts.
+
+    Q [B,Hq,L,d]; K, V [B,Hkv,L,d]; CK, CV [B,Hkv,>=n_core(max ts),d].
+    Returns O [B,Hq,len(ts),d] in fp64.  Each row t uses its own index sets:
+    cores 0..n_core(t)-1 then raw positions win_lo(t)..t, under one softmax.
+    """
+    B, Hq, _, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    ts = list(ts)
+    out = np.empty((B, Hq, len(ts), d))
+    scale = 1.0 / math.sqrt(d)
+    for i, t in enumerate(ts):
+        nc, lo = n_core(t, g, w), win_lo(t, w)
+        keys = np.concatenate([_f64(CK[:, :, :nc, :]), _f64(K[:, :, lo : t + 1, :])], axis=2)
+        vals = np.concatenate([_f64(CV[:, :, :nc, :]), _f64(V[:, :, lo : t + 1, :])], axis=2)
+        q = _f64(Q[:, :, t, :]).reshape(B, Hkv, G, d)          # R-9: head h -> kv head h//G
+        s = np.einsum("bhgd,bhnd->bhgn", q, keys) * scale
+        p = _softmax(s, axis=-1)
+        out[:, :, i, :] = np.einsum("bhgn,bhnd->bhgd", p, vals).reshape(B, Hq, d)
+    return out
+
+
+def attn_prefill(Q, K, V, CK, CV, g: int, w: int):
+    """All L rows of causal prefill (see ``attn_rows``)."""
+    return attn_rows(Q, K, V, CK, CV, g, w, range(Q.shape[2]))
+
+
+def attn_row(Q, K, V, CK, CV, g: int, w: int, t: int):
+    """Row t for every (batch, query head): O [B,Hq,d]."""
+    return attn_rows(Q, K, V, CK, CV, g, w, [t])[:, :, 0, :]
+
+
+def attn_decode(q_t, K_seq, V_seq, CK, CV, pos, g: int, w: int):
+    """One decode step (R-10): for batch b the new token sits at position pos[b].
+
+    q_t [B,Hq,d]; K_seq, V_seq [B,Hkv,T,d] hold every token up to and including
+    pos[b] for each b; CK, CV [B,Hkv,>=n_core(pos[b]),d] are the cores of the
+    completed groups of that sequence.  Row pos[b] of prefill over the extended
+    sequence is exactly this; returns [B,Hq,d] in fp64.
+    """
+    B, Hq, d = q_t.shape
+    out = np.empty((B, Hq, d))
+    for b in range(B):
+        t = int(pos[b])
+        Qb = np.zeros((1, Hq, t + 1, d))
+        Qb[0, :, t, :] = _f64(q_t[b])
+        out[b] = attn_rows(Qb, K_seq[b : b + 1], V_seq[b : b + 1], CK[b : b + 1], CV[b : b + 1],
+                           g, w, [t])[0, :, 0, :]
+    return out
+
