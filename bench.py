@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the CCA attention hot path on one MI355X.
+
+A step is one pass of the prefill hot path over the LLaMA-3.1-8B GQA workload
+(batch 1, 32 query / 8 kv heads, head dim 128, L = 131072, g = 16, w = 1024,
+bf16): cca_pool_core then cca_attn_prefill, inputs already resident in HBM.
+The decode workload (batch 8, 32/8 heads, 65536 cached tokens, 256 single-token
+steps) is timed in the same run and reported under "decode".
+
+Prints ONE JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
+--warmup W, --no-cpu (skip the CPU-oracle baseline), --no-decode.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import cca_inputs  # noqa: E402
+
+METRIC = "CCA prefill tokens/s + MFMA util at 128K (8B GQA shape, 1 GPU); decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+
+
+def visible_pairs(L, g, w):
+    t = np.arange(L, dtype=np.int64)
+    nc = np.where(t - w + 1 > 0, (t - w + 1) // g, 0)
+    lo = np.maximum(0, t - w + 1)
+    return int(nc.sum() + (t - lo + 1).sum())
+
+
+def prefill_flops(cfg):
+    """Algorithmic FLOPs: 4*d per visible (query head, key) pair (Q.K and P.V)."""
+    return 4.0 * cfg.d * cfg.B * cfg.Hq * visible_pairs(cfg.L, cfg.g, cfg.w)
+
+
+def pool_bytes(cfg):
+    """Algorithmic bytes of pooling: K and V read once, the G query rows at
+    each group end, core K and V written."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    m = cfg.L // cfg.g
+    return es * cfg.B * (2 * cfg.Hkv * m * cfg.g * cfg.d + cfg.Hq * m * cfg.d + 2 * cfg.Hkv * m * cfg.d)
+
+
+def decode_step_bytes(cfg, t):
+    """Algorithmic bytes of one decode step at position t for every sequence:
+    visible core + window K/V, q, out, k_t/v_t read and appended, and on a
+    group boundary the g-1 ring rows pooled plus the core written."""
+    es = 2
+    B, Hq, Hkv, d, g, w = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.g, cfg.w
+    nc = max(0, (t - w + 1) // g) if t - w + 1 > 0 else 0
+    nvis = nc + (t - max(0, t - w + 1) + 1)
+    by = B * Hkv * nvis * 2 * d * es          # K and V of visible keys
+    by += 2 * B * Hq * d * es                 # q_t in, out
+    by += 2 * 2 * B * Hkv * d * es            # k_t, v_t read + written to the ring
+    if (t + 1) % g == 0:
+        by += B * Hkv * ((g - 1) * 2 * d * es + 2 * d * es)
+    return by
+
+
+def cpu_oracle_baseline(cfg, q, k, v, budget_s=20.0):
+    """Times the fp64 CPU oracle (as it stands) on a bounded sample of the
+    prefill workload: pooling of one kv head over all L tokens (scaled to all
+    kv heads) plus the attention rows of the last S positions for every query
+    head; S doubles until the sample costs about budget_s/2."""
+    import oracle.cca_oracle as orc
+    try:
+        from threadpoolctl import threadpool_limits
+        cores = len(os.sched_getaffinity(0))
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # pragma: no cover
+        cores, limiter = os.cpu_count(), None
+    Q = q.to(torch.float32).numpy()
+    K = k.to(torch.float32).numpy()
+    V = v.to(torch.float32).numpy()
+    G = cfg.Hq // cfg.Hkv
+    # cores of every kv head are needed by the attention rows; the first one is timed
+    CKs = np.empty((cfg.B, cfg.Hkv, cfg.L // cfg.g, cfg.d))
+    CVs = np.empty_like(CKs)
+    t_pool_one = 0.0
+    for hk in range(cfg.Hkv):
+        t0 = time.perf_counter()
+        a, b_, _ = orc.pool_core(Q[:, hk * G:(hk + 1) * G], K[:, hk:hk + 1], V[:, hk:hk + 1], cfg.g)
+        if hk == 0:
+            t_pool_one = time.perf_counter() - t0
+        CKs[:, hk], CVs[:, hk] = a[:, 0], b_[:, 0]
+    t_pool = t_pool_one * cfg.Hkv
+    S, t_rows = 4, 0.0
+    while True:
+        rows = list(range(cfg.L - S, cfg.L))
+        t0 = time.perf_counter()
+        orc.attn_rows(Q, K, V, CKs, CVs, cfg.g, cfg.w, rows)
+        t_rows = time.perf_counter() - t0
+        if t_rows > budget_s / 4 or S >= 4096:
+            break
+        S *= 2
+    if limiter is not None and hasattr(limiter, "unregister"):
+        limiter.unregister()
+    per_token = t_rows / S + t_pool / cfg.L
+    return {
+        "value": 1.0 / per_token,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: pooling of 1 of {cfg.Hkv} kv heads over all {cfg.L} tokens "
+                   f"({t_pool_one:.2f} s, scaled x{cfg.Hkv}) + attention rows of the last {S} positions "
+                   f"for all {cfg.Hq} query heads ({t_rows:.2f} s); last positions see the most keys, "
+                   f"so this rate is a lower bound for the whole sequence"),
+    }
+
+
+def bench_decode(cca, cfg, steps_timed=True):
+    """256 sequential decode steps over a 65536-token cache; one timed region."""
+    B, Hq, Hkv, d, g, w, L, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.g, cfg.w, cfg.L, cfg.decode_steps
+    dev = "cuda:0"
+    x = cca_inputs.decode_inputs(cfg)
+    R, m_cap = w, (L + S) // g
+    kd, vd = x["k"].to(dev), x["v"].to(dev)
+    qfull = torch.zeros((B, Hq, L, d), dtype=torch.bfloat16, device=dev)
+    qfull[:, :, g - 1::g] = x["q_ends"].to(dev)
+    ck = torch.zeros((B, Hkv, m_cap, d), dtype=torch.bfloat16, device=dev)
+    cv = torch.zeros_like(ck)
+    cca.cca_pool_core(qfull, kd[:, :, :L].contiguous(), vd[:, :, :L].contiguous(), ck, cv, g)
+    del qfull
+    rk = torch.empty((B, Hkv, R, d), dtype=torch.bfloat16, device=dev)
+    rv = torch.empty_like(rk)
+    slots = torch.arange(L - R, L, device=dev) % R
+    rk[:, :, slots] = kd[:, :, L - R:L]
+    rv[:, :, slots] = vd[:, :, L - R:L]
+    ring0 = (rk.clone(), rv.clone())
+    pos = torch.full((B,), L, dtype=torch.int32, device=dev)
+    ws = torch.empty(cca.cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+    qs = x["q_steps"].to(dev).permute(2, 0, 1, 3).contiguous()     # [S, B, Hq, d]
+    ks = kd[:, :, L:L + S].permute(2, 0, 1, 3).contiguous()         # [S, B, Hkv, d]
+    vs = vd[:, :, L:L + S].permute(2, 0, 1, 3).contiguous()
+
+    def run_all():
+        for i in range(S):
+            cca.cca_attn_decode(qs[i], ks[i], vs[i], rk, rv, ck, cv, pos, out, ws, g, w, advance_pos=True)
+
+    def reset():
+        pos.fill_(L)
+        rk.copy_(ring0[0])
+        rv.copy_(ring0[1])
+
+    run_all()          # warm-up pass
+    reset()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run_all()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert pos.tolist() == [L + S] * B
+    assert torch.isfinite(out.float()).all()
+    total_bytes = sum(decode_step_bytes(cfg, L + i) for i in range(S))
+    gbs = total_bytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": cfg.name,
+        "steps": S,
+        "us_per_step": ms * 1e3 / S,
+        "GB_per_s": gbs,
+        "hbm_frac": gbs / PEAK_HBM_GBS,
+        "algorithmic_bytes_per_step": total_bytes / S,
+        "launches_per_step": 2,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no sharding or collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import sparse_long_context_cca_amd as cca
+    cca.load()
+    dev = "cuda:0"
+    cfg = cca_inputs.CONFIGS[4]
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    m = cfg.L // cfg.g
+    ck = torch.empty((cfg.B, cfg.Hkv, m, cfg.d), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        cca.cca_pool_core(qd, kd, vd, ck, cv, cfg.g)
+        if ev is not None:
+            ev[0].record(stream)
+        cca.cca_attn_prefill(qd, kd, vd, ck, cv, out, cfg.g, cfg.w)
+        if ev is not None:
+            ev[1].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    prefill_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = total_ms / args.steps
+    prefill_avg = sum(prefill_ms) / len(prefill_ms)
+    pool_ms = ms_step - prefill_avg
+    assert torch.isfinite(out[0, :, -4:].float()).all()
+
+    flops = prefill_flops(cfg)
+    tflops = flops / (prefill_avg * 1e-3) / 1e12
+    tokens = cfg.B * cfg.L
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. normal Q/K/V, bf16)",
+        "config": {"workload": cfg.name, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+                   "seq_len": cfg.L, "head_dim": cfg.d, "group": cfg.g, "window": cfg.w},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "prefill_mfma_kernel<128,1>",
+            "achieved": tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_ms": prefill_avg,
+        },
+        "pool": {"ms": pool_ms, "algorithmic_bytes": pool_bytes(cfg),
+                 "GB_per_s": pool_bytes(cfg) / (pool_ms * 1e-3) / 1e9 if pool_ms > 0 else None},
+    }
+    if not args.no_decode:
+        del qd, kd, vd, out, ck, cv
+        torch.cuda.empty_cache()
+        print("[bench] decode", file=sys.stderr, flush=True)
+        result["decode"] = bench_decode(cca, cca_inputs.CONFIGS[5])
+    if not args.no_cpu:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_oracle_baseline(cfg, q, k, v)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * cca.h - C ABI of the Core Context Aware (CCA) attention forward on AMD
+ * MI355X (gfx950).
+ *
+ * The method (Core Context Aware Transformers for Long Context Language
+ * Modeling):
+ *   - global-aware pooling: tokens are cut into non-overlapping groups of g;
+ *     each group becomes one core key/value pair, weighted by a softmax of the
+ *     group's last query against the group's keys (digest at
+ *     digest.lyk-ai.com/posts/2412.12465, "Method", pooling formula; ICML 2025
+ *     article at changsha.jmyizhao.com, global-aware pooling paragraph);
+ *   - locality-preserving module: each token also sees the raw keys of its last
+ *     w tokens (same article, locality-preserving module paragraph);
+ *   - fusion: one softmax over [visible core tokens ; raw window] (digest,
+ *     "Method", fusion formula; paper card at atlas.scime.ai, "Approach").
+ *
+ * Visibility (the pages name the index sets but do not define them; this
+ * library fixes them as): query t sees raw positions max(0, t-w+1) .. t and the
+ * core of every group j whose last token (j+1)g-1 < t-w+1, i.e.
+ *   n_core(t) = max(0, floor((t-w+1)/g)),  win_lo(t) = max(0, t-w+1).
+ * Groups start at token 0; a trailing partial group has no core.
+ * GQA: one core pair per (kv head, group); its pooling query is the mean over
+ * the G = Hq/Hkv query heads of that kv head of their last-token queries.
+ * Query head h reads kv head h / G.  Softmax scale is 1/sqrt(d) everywhere.
+ *
+ * Conventions shared by every entry point:
+ *   - Layouts are row-major with the head dimension d contiguous:
+ *       Q, O        [B, Hq, L, d]      K, V          [B, Hkv, L, d]
+ *       core K/V    [B, Hkv, m_cap, d] (slot j = group j)
+ *   - Every pointer argument except `stream` is a DEVICE pointer, 16-byte
+ *     aligned.  The caller allocates and frees all memory (including the decode
+ *     workspace) and owns the stream; the library never allocates, frees or
+ *     synchronises.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; results are valid once the stream has been synchronised.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and a status other than CCA_OK is returned,
+ *     with a message available from cca_last_error() (per thread).
+ *   - Input dtype `dt` applies to q, k, v and the core/ring caches.
+ *     Supported: d in {64, 128}; dt in {CCA_F32, CCA_BF16}; out_dt in
+ *     {dt, CCA_F32}.  Sizes must keep every buffer below 2^31 elements.
+ *   - Rounding: accumulation is fp32; core K/V and outputs are rounded to their
+ *     storage dtype once, to nearest even.  bf16 attention feeds the matrix
+ *     cores bf16 operands (probabilities are rounded to bf16 before P*V).
+ */
+#ifndef CCA_H
+#define CCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cca_status {
+  CCA_OK = 0,
+  CCA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, bad enum */
+  CCA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, dtype combination, Hq % Hkv != 0 */
+  CCA_ERR_CAPACITY = 3,    /* m_cap < L/g, ring R < max(w, g), workspace too small */
+  CCA_ERR_HIP = 4          /* a HIP launch failed; see cca_last_error() */
+} cca_status;
+
+typedef enum cca_dtype { CCA_F32 = 0, CCA_BF16 = 1 } cca_dtype;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int cca_version(void);
+
+/* Static string for a status code. */
+const char* cca_status_string(int status);
+
+/* Message of the last error returned on the calling thread ("" if none). */
+const char* cca_last_error(void);
+
+/*
+ * cca_visibility_table - integer index tables of the visibility rule above.
+ *   n_core[t] and win_lo[t] for t < L (int32 [L]); group_last[j] = (j+1)g-1
+ *   for j < L/g (int32 [L/g]; may be NULL when L < g).
+ * Bit-exact by construction; the kernels use the same device index functions.
+ */
+cca_status cca_visibility_table(int L, int g, int w, int32_t* n_core, int32_t* win_lo,
+                                int32_t* group_last, void* stream);
+
+/*
+ * cca_pool_core - global-aware pooling (digest, "Method", pooling formula).
+ *   For every (b, kv head, group j < m = L/g):
+ *     qbar = mean over the G query heads of Q[b, h, (j+1)g-1, :]
+ *     a    = softmax_tau(qbar . K[b, kv, jg+tau, :] / sqrt(d)), tau < g
+ *     core_k[b, kv, j, :] = sum_tau a_tau K[b, kv, jg+tau, :]   (same for V)
+ *   q [B,Hq,L,d], k/v [B,Hkv,L,d] (dt); core_k/core_v [B,Hkv,m_cap,d] (dt),
+ *   slots j < m written, others untouched.  weights: NULL, or fp32
+ *   [B,Hkv,m,g] receiving a (for tests).
+ * Errors: INVALID_ARG (null, L<1, g<1, B/Hq/Hkv<1), UNSUPPORTED (d, dt,
+ *   Hq % Hkv), CAPACITY (m_cap < m).
+ */
+cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core_k, void* core_v,
+                         int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d, int g,
+                         cca_dtype dt, void* stream);
+
+/*
+ * cca_attn_prefill - causal prefill of the fused CCA attention (digest,
+ * "Method", fusion formula): for every (b, h, t < L)
+ *     keys   = [core_k[0 .. n_core(t)) ; K[win_lo(t) .. t]]   (values alike)
+ *     out[b,h,t,:] = softmax(q_t . keys^T / sqrt(d)) . values
+ *   core_k/core_v: [B,Hkv,m_cap,d] as written by cca_pool_core (slots < L/g
+ *   are read).  out: [B,Hq,L,d] in out_dt.
+ * Errors: as cca_pool_core, plus INVALID_ARG for w < 1 or a bad out_dt.
+ */
+cca_status cca_attn_prefill(const void* q, const void* k, const void* v, const void* core_k,
+                            const void* core_v, int m_cap, void* out, cca_dtype out_dt, int B,
+                            int Hq, int Hkv, int L, int d, int g, int w, cca_dtype dt,
+                            void* stream);
+
+/*
+ * cca_attn_prefill_ex - cca_attn_prefill with an explicit kernel choice, for
+ * tests: kernel 0 = automatic (bf16: matrix-core kernel; fp32: vector
+ * kernel), 1 = fp32 vector kernel (any dt), 2 = bf16 matrix-core kernel.
+ * UNSUPPORTED if the choice does not fit dt.
+ */
+cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, const void* core_k,
+                               const void* core_v, int m_cap, void* out, cca_dtype out_dt, int B,
+                               int Hq, int Hkv, int L, int d, int g, int w, cca_dtype dt,
+                               int kernel, void* stream);
+
+/*
+ * cca_decode_workspace_bytes - size of the workspace cca_attn_decode needs for
+ * these shapes (fp32 partial softmax states of its split-K pass).
+ */
+size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int g, int w);
+
+/*
+ * cca_attn_decode - one KV-cached decode step for a batch (CCA supports a KV
+ * cache natively, per the article).  For batch b the new token has position
+ * t = pos[b] (tokens already cached); every sequence may sit at its own t.
+ *   q_t [B,Hq,d], k_t/v_t [B,Hkv,d] (dt): the new token's projections.
+ *   ring_k/ring_v [B,Hkv,R,d] (dt): raw keys/values, position p in slot p % R;
+ *     must hold positions max(0, t-R+1) .. t-1.  R >= max(w, g).
+ *   core_k/core_v [B,Hkv,m_cap,d] (dt): cores of every completed group.
+ *   Enqueued work: (1) k_t/v_t are written to slot t % R; (2) when (t+1) % g
+ *   == 0, group (t+1)/g-1 is pooled from positions t-g+1 .. t with the mean
+ *   over its G heads of q_t and written to core slot (t+1)/g-1 (it is not yet
+ *   visible to t); (3) out[b,h,:] = softmax over the n_core(t) cores and the
+ *   raw window win_lo(t) .. t (the same row prefill computes for position t).
+ *   out: [B,Hq,d] in out_dt.  workspace: device memory of at least
+ *   cca_decode_workspace_bytes(...) bytes, contents need no initialisation.
+ *   pos: int32 [B] device array; read, and incremented by one after the step
+ *   when advance_pos != 0 (so that a step can be replayed in a loop).
+ *   A sequence with t < 0 or floor((t+1)/g) > m_cap (no core slot left) gets
+ *   NaN outputs and no cache writes (pos lives on the device, so this cannot
+ *   be reported as a status).
+ * Errors: INVALID_ARG, UNSUPPORTED as above; CAPACITY when R < max(w, g) or
+ *   the workspace is too small.
+ */
+cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                           void* ring_v, int R, void* core_k, void* core_v, int m_cap,
+                           int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                           void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
+                           int g, int w, cca_dtype dt, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCA_H */

@@ -22,5 +22,5 @@ the pages ("parity unpinned"), are listed in ``cca_oracle``'s module docstring.
 """
 from .cca_oracle import (  # noqa: F401
     n_core, win_lo, visibility, visible_pairs_total, cache_tokens,
-    pool_core, attn_prefill, attn_row, attn_decode, attn_rows,
+    pool_core, pool_from_last, attn_prefill, attn_row, attn_decode, attn_rows, attn_rows_q,
 )

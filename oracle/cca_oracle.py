@@ -128,23 +128,35 @@ def pool_core(Q, K, V, g: int):
     Returns CK, CV [B,Hkv,m,d] and the pooling weights A [B,Hkv,m,g], m = L//g.
     """
     B, Hq, L, d = Q.shape
+    m = L // g
+    last = np.array([group_last(j, g) for j in range(m)], dtype=np.int64)
+    # query of each group's last token, one per query head: [B,Hq,m,d]
+    return pool_from_last(Q[:, :, last, :], K, V, g)
+
+
+def pool_from_last(q_last, K, V, g: int):
+    """Pooling given the last-token query rows: q_last[:, h, j] is the query of
+    head h at token (j+1)g-1.  Same outputs as ``pool_core``."""
+    B, Hq, m, d = q_last.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
-    m = L // g
     if m == 0:
         z = np.zeros((B, Hkv, 0, d))
         return z, z.copy(), np.zeros((B, Hkv, 0, g))
-    last = np.array([group_last(j, g) for j in range(m)])
-    # query of each group's last token, one per query head: [B,Hq,m,d]
-    q_last = _f64(Q[:, :, last, :])
-    # R-8: one pooling query per kv head = mean over its G query heads
-    q_bar = q_last.reshape(B, Hkv, G, m, d).mean(axis=2)
-    Kg = _f64(K[:, :, : m * g, :]).reshape(B, Hkv, m, g, d)
-    Vg = _f64(V[:, :, : m * g, :]).reshape(B, Hkv, m, g, d)
-    s = np.einsum("bhmd,bhmtd->bhmt", q_bar, Kg) / math.sqrt(d)
-    A = _softmax(s, axis=-1)
-    CK = np.einsum("bhmt,bhmtd->bhmd", A, Kg)
-    CV = np.einsum("bhmt,bhmtd->bhmd", A, Vg)
+    CK = np.empty((B, Hkv, m, d))
+    CV = np.empty((B, Hkv, m, d))
+    A = np.empty((B, Hkv, m, g))
+    for b in range(B):
+        for hk in range(Hkv):
+            # R-8: one pooling query per kv head = mean over its G query heads
+            q_bar = _f64(q_last[b, hk * G : hk * G + G]).mean(axis=0)         # [m, d]
+            Kg = _f64(K[b, hk, : m * g, :]).reshape(m, g, d)                  # group i = rows ig..ig+g-1
+            Vg = _f64(V[b, hk, : m * g, :]).reshape(m, g, d)
+            s = (Kg * q_bar[:, None, :]).sum(axis=-1) / math.sqrt(d)          # [m, g]
+            a = _softmax(s, axis=-1)
+            A[b, hk] = a
+            CK[b, hk] = (a[:, :, None] * Kg).sum(axis=1)
+            CV[b, hk] = (a[:, :, None] * Vg).sum(axis=1)
     return CK, CV, A
 
 
@@ -155,23 +167,34 @@ def attn_rows(Q, K, V, CK, CV, g: int, w: int, ts):
     """Fused attention rows ([digest], Method, fusion formula) for positions ts.
 
     Q [B,Hq,L,d]; K, V [B,Hkv,L,d]; CK, CV [B,Hkv,>=n_core(max ts),d].
-    Returns O [B,Hq,len(ts),d] in fp64.  Each row t uses its own index sets:
-    cores 0..n_core(t)-1 then raw positions win_lo(t)..t, under one softmax.
+    Returns O [B,Hq,len(ts),d] in fp64.
     """
-    B, Hq, _, d = Q.shape
+    ts = list(ts)
+    return attn_rows_q(Q[:, :, ts, :], K, V, CK, CV, g, w, ts)
+
+
+def attn_rows_q(qrows, K, V, CK, CV, g: int, w: int, ts):
+    """As ``attn_rows`` with the query rows given: qrows[:, :, i] sits at ts[i].
+
+    Each row t uses its own index sets: cores 0..n_core(t)-1 and raw positions
+    win_lo(t)..t; the scores of both parts are concatenated and go through ONE
+    softmax, and the output is the probability-weighted sum of both parts'
+    values.
+    """
+    B, Hq, _, d = qrows.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
-    ts = list(ts)
     out = np.empty((B, Hq, len(ts), d))
     scale = 1.0 / math.sqrt(d)
     for i, t in enumerate(ts):
         nc, lo = n_core(t, g, w), win_lo(t, w)
-        keys = np.concatenate([_f64(CK[:, :, :nc, :]), _f64(K[:, :, lo : t + 1, :])], axis=2)
-        vals = np.concatenate([_f64(CV[:, :, :nc, :]), _f64(V[:, :, lo : t + 1, :])], axis=2)
-        q = _f64(Q[:, :, t, :]).reshape(B, Hkv, G, d)          # R-9: head h -> kv head h//G
-        s = np.einsum("bhgd,bhnd->bhgn", q, keys) * scale
-        p = _softmax(s, axis=-1)
-        out[:, :, i, :] = np.einsum("bhgn,bhnd->bhgd", p, vals).reshape(B, Hq, d)
+        q = _f64(qrows[:, :, i, :]).reshape(B, Hkv, G, d)       # R-9: head h -> kv head h//G
+        ck, cv = _f64(CK[:, :, :nc, :]), _f64(CV[:, :, :nc, :])
+        kw, vw = _f64(K[:, :, lo : t + 1, :]), _f64(V[:, :, lo : t + 1, :])
+        s = np.concatenate([q @ ck.transpose(0, 1, 3, 2), q @ kw.transpose(0, 1, 3, 2)], axis=-1) * scale
+        p = _softmax(s, axis=-1)                                  # one softmax over [cores ; window]
+        o = p[..., :nc] @ cv + p[..., nc:] @ vw
+        out[:, :, i, :] = o.reshape(B, Hq, d)
     return out
 
 
@@ -197,9 +220,6 @@ def attn_decode(q_t, K_seq, V_seq, CK, CV, pos, g: int, w: int):
     out = np.empty((B, Hq, d))
     for b in range(B):
         t = int(pos[b])
-        Qb = np.zeros((1, Hq, t + 1, d))
-        Qb[0, :, t, :] = _f64(q_t[b])
-        out[b] = attn_rows(Qb, K_seq[b : b + 1], V_seq[b : b + 1], CK[b : b + 1], CV[b : b + 1],
-                           g, w, [t])[0, :, 0, :]
+        out[b] = attn_rows_q(q_t[b : b + 1, :, None, :], K_seq[b : b + 1], V_seq[b : b + 1],
+                             CK[b : b + 1], CV[b : b + 1], g, w, [t])[0, :, 0, :]
     return out
-

@@ -1,0 +1,10 @@
+"""CCA (Core Context Aware) attention forward for AMD MI355X (gfx950).
+
+The computation lives in libcca.so (hand-written HIP kernels behind the C ABI
+of include/cca.h); this package only marshals torch tensors into that ABI.
+"""
+from ._lib import (  # noqa: F401
+    CCA_BF16, CCA_ERR_CAPACITY, CCA_ERR_HIP, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_F32,
+    CCA_OK, CCAError, EXPORTS, LIB_PATH, cca_attn_decode, cca_attn_prefill,
+    cca_decode_workspace_bytes, cca_pool_core, cca_version, cca_visibility_table, load,
+)

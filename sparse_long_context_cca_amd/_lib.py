@@ -1,0 +1,144 @@
+"""ctypes binding of libcca.so (declared in include/cca.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if libcca.so is missing or does not load,
+importing the entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcca.so")
+
+CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_CAPACITY, CCA_ERR_HIP = range(5)
+CCA_F32, CCA_BF16 = 0, 1
+
+EXPORTS = ["cca_version", "cca_status_string", "cca_last_error", "cca_visibility_table",
+           "cca_pool_core", "cca_attn_prefill", "cca_attn_prefill_ex", "cca_decode_workspace_bytes",
+           "cca_attn_decode"]
+
+
+class CCAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libcca.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_long_context_cca_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "cca_version": ([], I),
+        "cca_status_string": ([I], ctypes.c_char_p),
+        "cca_last_error": ([], ctypes.c_char_p),
+        "cca_visibility_table": ([I, I, I, P, P, P, P], I),
+        "cca_pool_core": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, P], I),
+        "cca_attn_prefill": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, P], I),
+        "cca_attn_prefill_ex": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, P], I),
+        "cca_decode_workspace_bytes": ([I, I, I, I, I, I, I], S),
+        "cca_attn_decode": ([P, P, P, P, P, I, P, P, I, P, I, P, I, P, S, I, I, I, I, I, I, I, P], I),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def status_name(status: int) -> str:
+    return load().cca_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != CCA_OK:
+        raise CCAError(status, load().cca_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CCA_F32
+    if t.dtype == torch.bfloat16:
+        return CCA_BF16
+    raise CCAError(CCA_ERR_UNSUPPORTED, f"dtype {t.dtype} not supported")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise CCAError(CCA_ERR_INVALID_ARG, "tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------ entry points
+
+
+def cca_version() -> int:
+    return load().cca_version()
+
+
+def cca_visibility_table(L: int, g: int, w: int, n_core: torch.Tensor, win_lo: torch.Tensor,
+                         group_last: torch.Tensor | None, stream=None) -> None:
+    _check(load().cca_visibility_table(L, g, w, _ptr(n_core), _ptr(win_lo), _ptr(group_last),
+                                       _stream(stream)))
+
+
+def cca_pool_core(q, k, v, core_k, core_v, g: int, weights=None, stream=None) -> None:
+    """q [B,Hq,L,d]; k, v [B,Hkv,L,d]; core_k, core_v [B,Hkv,m_cap,d]; weights fp32 [B,Hkv,L//g,g]."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    m_cap = core_k.shape[2] if core_k is not None else 0
+    _check(load().cca_pool_core(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
+                                _ptr(weights), B, Hq, Hkv, L, d, g, _dt(q), _stream(stream)))
+
+
+def cca_attn_prefill(q, k, v, core_k, core_v, out, g: int, w: int, kernel: int = 0,
+                     stream=None) -> None:
+    """out [B,Hq,L,d] in q's dtype or fp32; kernel: 0 auto, 1 vector-ALU, 2 matrix-core."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    m_cap = core_k.shape[2] if core_k is not None else 0
+    _check(load().cca_attn_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
+                                      _ptr(out), _dt(out), B, Hq, Hkv, L, d, g, w, _dt(q), kernel,
+                                      _stream(stream)))
+
+
+def cca_decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, m_cap: int, g: int, w: int) -> int:
+    return int(load().cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w))
+
+
+def cca_attn_decode(q_t, k_t, v_t, ring_k, ring_v, core_k, core_v, pos, out, workspace, g: int,
+                    w: int, advance_pos: bool = False, stream=None) -> None:
+    """q_t [B,Hq,d]; k_t, v_t [B,Hkv,d]; ring_* [B,Hkv,R,d]; core_* [B,Hkv,m_cap,d];
+    pos int32 [B]; out [B,Hq,d]; workspace uint8 of cca_decode_workspace_bytes bytes."""
+    B, Hq, d = q_t.shape
+    Hkv = k_t.shape[1]
+    R = ring_k.shape[2]
+    m_cap = core_k.shape[2]
+    _check(load().cca_attn_decode(_ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(ring_k), _ptr(ring_v), R,
+                                  _ptr(core_k), _ptr(core_v), m_cap, _ptr(pos), int(advance_pos),
+                                  _ptr(out), _dt(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, g, w,
+                                  _dt(q_t), _stream(stream)))

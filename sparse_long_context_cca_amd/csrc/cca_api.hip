@@ -1,0 +1,224 @@
+// C ABI of the CCA attention library: argument validation on the host, then
+// kernel launches on the caller's stream.  Nothing here allocates memory or
+// synchronises.  See include/cca.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdarg>
+#include <string>
+
+#include "../../include/cca.h"
+#include "cca_device.hpp"
+#include "cca_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cca_status fail(cca_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+cca_status ok() {
+  g_last_error.clear();
+  return CCA_OK;
+}
+
+cca_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+const long long kMaxElems = (1LL << 31) - 1;
+
+#define REQUIRE_PTR(p)                                                                  \
+  do {                                                                                  \
+    if ((p) == nullptr) return fail(CCA_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);     \
+    if (!aligned16(p)) return fail(CCA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, #p); \
+  } while (0)
+
+// Checks shared by every entry point that takes a head layout.
+cca_status check_heads(const char* fn, int B, int Hq, int Hkv, int d, int dt) {
+  if (B < 1 || Hq < 1 || Hkv < 1)
+    return fail(CCA_ERR_INVALID_ARG, "%s: B=%d Hq=%d Hkv=%d must be >= 1", fn, B, Hq, Hkv);
+  if (dt != CCA_F32 && dt != CCA_BF16)
+    return fail(CCA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dt);
+  if (Hq % Hkv != 0)
+    return fail(CCA_ERR_UNSUPPORTED, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (d != 64 && d != 128) return fail(CCA_ERR_UNSUPPORTED, "%s: head dim d=%d not in {64,128}", fn, d);
+  return CCA_OK;
+}
+
+cca_status check_out_dt(const char* fn, int out_dt, int dt) {
+  if (out_dt != CCA_F32 && out_dt != CCA_BF16)
+    return fail(CCA_ERR_INVALID_ARG, "%s: unknown out dtype %d", fn, out_dt);
+  if (out_dt != dt && out_dt != CCA_F32)
+    return fail(CCA_ERR_UNSUPPORTED, "%s: out dtype must be the input dtype or fp32", fn);
+  return CCA_OK;
+}
+
+cca_status check_sizes(const char* fn, long long a, long long b, long long c) {
+  if (a > kMaxElems || b > kMaxElems || c > kMaxElems)
+    return fail(CCA_ERR_UNSUPPORTED, "%s: a buffer exceeds 2^31-1 elements", fn);
+  return CCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cca_version(void) { return 100; }
+
+const char* cca_status_string(int status) {
+  switch (status) {
+    case CCA_OK: return "CCA_OK";
+    case CCA_ERR_INVALID_ARG: return "CCA_ERR_INVALID_ARG";
+    case CCA_ERR_UNSUPPORTED: return "CCA_ERR_UNSUPPORTED";
+    case CCA_ERR_CAPACITY: return "CCA_ERR_CAPACITY";
+    case CCA_ERR_HIP: return "CCA_ERR_HIP";
+    default: return "CCA_ERR_UNKNOWN";
+  }
+}
+
+const char* cca_last_error(void) { return g_last_error.c_str(); }
+
+cca_status cca_visibility_table(int L, int g, int w, int32_t* n_core, int32_t* win_lo,
+                                int32_t* group_last, void* stream) {
+  const char* fn = "cca_visibility_table";
+  if (L < 1 || g < 1 || w < 1)
+    return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
+  REQUIRE_PTR(n_core);
+  REQUIRE_PTR(win_lo);
+  if (L / g > 0) REQUIRE_PTR(group_last);
+  return from_hip(cca::launch_visibility(L, g, w, n_core, win_lo, group_last,
+                                         static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core_k, void* core_v,
+                         int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d, int g,
+                         cca_dtype dt, void* stream) {
+  const char* fn = "cca_pool_core";
+  if (L < 1 || g < 1) return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d must be >= 1", fn, L, g);
+  cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  const int m = L / g;
+  if (m_cap < m) return fail(CCA_ERR_CAPACITY, "%s: m_cap=%d < L/g=%d", fn, m_cap, m);
+  st = check_sizes(fn, (long long)B * Hq * L * d, (long long)B * Hkv * L * d,
+                   (long long)B * Hkv * m_cap * d);
+  if (st != CCA_OK) return st;
+  if (m == 0) return ok();  // no complete group: nothing to write
+  REQUIRE_PTR(core_k);
+  REQUIRE_PTR(core_v);
+  if (weights != nullptr && !aligned16(weights))
+    return fail(CCA_ERR_INVALID_ARG, "%s: weights is not 16-byte aligned", fn);
+  cca::Shape sh{B, Hq, Hkv, L, d, g, 1};
+  return from_hip(cca::launch_pool(q, k, v, core_k, core_v, m_cap, weights, sh, dt,
+                                   static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, const void* core_k,
+                               const void* core_v, int m_cap, void* out, cca_dtype out_dt, int B,
+                               int Hq, int Hkv, int L, int d, int g, int w, cca_dtype dt,
+                               int kernel, void* stream) {
+  const char* fn = "cca_attn_prefill";
+  if (L < 1 || g < 1 || w < 1)
+    return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
+  cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_out_dt(fn, out_dt, dt);
+  if (st != CCA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  const int m = L / g;
+  if (m_cap < m) return fail(CCA_ERR_CAPACITY, "%s: m_cap=%d < L/g=%d", fn, m_cap, m);
+  // Cores are read only when some query sees one: n_core(L-1) > 0.
+  if (cca::n_core(L - 1, g, w) > 0) {
+    REQUIRE_PTR(core_k);
+    REQUIRE_PTR(core_v);
+  }
+  st = check_sizes(fn, (long long)B * Hq * L * d, (long long)B * Hkv * L * d,
+                   (long long)B * Hkv * m_cap * d);
+  if (st != CCA_OK) return st;
+  if (kernel < 0 || kernel > 2) return fail(CCA_ERR_INVALID_ARG, "%s: kernel=%d", fn, kernel);
+  if (kernel == 2 && dt != CCA_BF16)
+    return fail(CCA_ERR_UNSUPPORTED, "%s: the matrix-core kernel takes bf16 inputs", fn);
+  if (kernel == 0) kernel = (dt == CCA_BF16) ? 2 : 1;
+  cca::Shape sh{B, Hq, Hkv, L, d, g, w};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kernel == 2)
+    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, s), fn);
+  return from_hip(cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, dt, s),
+                  fn);
+}
+
+cca_status cca_attn_prefill(const void* q, const void* k, const void* v, const void* core_k,
+                            const void* core_v, int m_cap, void* out, cca_dtype out_dt, int B,
+                            int Hq, int Hkv, int L, int d, int g, int w, cca_dtype dt,
+                            void* stream) {
+  return cca_attn_prefill_ex(q, k, v, core_k, core_v, m_cap, out, out_dt, B, Hq, Hkv, L, d, g, w,
+                             dt, 0, stream);
+}
+
+size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int g, int w) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || d < 1 || m_cap < 0 || g < 1 || w < 1) return 0;
+  return cca::decode_plan(B, Hq, Hkv, d, m_cap, g, w).ws_bytes;
+}
+
+cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                           void* ring_v, int R, void* core_k, void* core_v, int m_cap,
+                           int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                           void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
+                           int g, int w, cca_dtype dt, void* stream) {
+  const char* fn = "cca_attn_decode";
+  if (g < 1 || w < 1) return fail(CCA_ERR_INVALID_ARG, "%s: g=%d w=%d must be >= 1", fn, g, w);
+  cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_out_dt(fn, out_dt, dt);
+  if (st != CCA_OK) return st;
+  REQUIRE_PTR(q_t);
+  REQUIRE_PTR(k_t);
+  REQUIRE_PTR(v_t);
+  REQUIRE_PTR(ring_k);
+  REQUIRE_PTR(ring_v);
+  REQUIRE_PTR(out);
+  if (m_cap < 0) return fail(CCA_ERR_INVALID_ARG, "%s: m_cap=%d", fn, m_cap);
+  if (m_cap > 0) {
+    REQUIRE_PTR(core_k);
+    REQUIRE_PTR(core_v);
+  }
+  if (pos == nullptr) return fail(CCA_ERR_INVALID_ARG, "%s: pos is NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(pos) & 3u) != 0)
+    return fail(CCA_ERR_INVALID_ARG, "%s: pos is not 4-byte aligned", fn);
+  const int need_r = w > g ? w : g;
+  if (R < need_r) return fail(CCA_ERR_CAPACITY, "%s: ring R=%d < max(w,g)=%d", fn, R, need_r);
+  st = check_sizes(fn, (long long)B * Hkv * R * d, (long long)B * Hkv * m_cap * d,
+                   (long long)B * Hq * d);
+  if (st != CCA_OK) return st;
+  cca::DecodePlan plan = cca::decode_plan(B, Hq, Hkv, d, m_cap, g, w);
+  if (workspace_bytes < plan.ws_bytes)
+    return fail(CCA_ERR_CAPACITY, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes,
+                plan.ws_bytes);
+  if (plan.ws_bytes > 0) REQUIRE_PTR(workspace);
+  cca::Shape sh{B, Hq, Hkv, 0, d, g, w};
+  return from_hip(cca::launch_decode(q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v, m_cap, pos,
+                                     advance_pos, out, out_dt, workspace, plan, sh, dt,
+                                     static_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+}  // extern "C"

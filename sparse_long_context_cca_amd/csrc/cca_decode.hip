@@ -1,0 +1,471 @@
+// KV-cached decode step of the fused CCA attention (the ICML 2025 article at
+// changsha.jmyizhao.com says CCA supports a KV cache natively and decodes at
+// FlashAttention-level speed; the digest at digest.lyk-ai.com/posts/2412.12465,
+// "Method", fusion formula, defines the row computed).
+//
+// Per step and sequence b (new token at position t = pos[b]):
+//   pass 1 (grid: splits x query-head groups x batch)
+//     - one block per (b, kv head) appends k_t, v_t to ring slot t % R and,
+//       when (t+1) % g == 0, pools group (t+1)/g-1 (positions t-g+1..t; the
+//       pooling query is the mean over the kv head's G query heads of q_t) into
+//       core slot (t+1)/g-1.  Neither location is read by this step: the ring
+//       slot held position t-R <= t-w, and the new core is not visible to t.
+//     - every block streams its share of the visible keys [cores 0..n_core(t)
+//       ; raw win_lo(t)..t] once from HBM and keeps an online softmax state for
+//       its query heads; position t itself is read from k_t/v_t.
+//     - the partial states (max, sum, weighted values) go to the workspace.
+//   pass 2 merges the split states per (b, query head), writes the output and
+//   optionally advances pos[b].
+// HBM-bound: every visible K/V byte is read once per step.
+#include "cca_device.hpp"
+#include "cca_internal.hpp"
+
+namespace cca {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBatch = 4;  // keys per lane group per iteration
+
+template <int DT>
+struct Slice;  // a lane's 16-byte slice of a row, as floats
+template <>
+struct Slice<0> {
+  static constexpr int N = 4;
+  static __device__ __forceinline__ void load(const void* p, float* x) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  }
+  static __device__ __forceinline__ void store(void* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+template <>
+struct Slice<1> {
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void load(const void* p, float* x) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void store(void* p, const float* x) {
+    uint4 v;
+    v.x = pack_bf16x2(x[0], x[1]);
+    v.y = pack_bf16x2(x[2], x[3]);
+    v.z = pack_bf16x2(x[4], x[5]);
+    v.w = pack_bf16x2(x[6], x[7]);
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+};
+
+__device__ __forceinline__ bool decode_valid(int t, int g, int m_cap) {
+  return t >= 0 && (t + 1) / g <= m_cap;
+}
+
+// Pools the group ending at t with one wave: rows t-g+1..t-1 from the ring,
+// row t from k_t/v_t; pooling query = mean of q_t over the kv head's G heads.
+template <int DT, int D>
+__device__ void pool_new_group(const char* q_t, const char* k_new, const char* v_new,
+                               const char* ring_k, const char* ring_v, char* ck, char* cv, int t,
+                               int R, int g, int G, float scale_log2) {
+  typedef Slice<DT> S;
+  constexpr int ES = DT == 0 ? 4 : 2;
+  constexpr int EPL = S::N;
+  constexpr int LPK = D * ES / 16;
+  constexpr int KPW = 64 / LPK;
+  const int lane = threadIdx.x & 63;
+  const int ks = lane / LPK;
+  const int d0 = (lane % LPK) * EPL;
+
+  float qbar[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qbar[e] = 0.f;
+  for (int gh = 0; gh < G; ++gh) {
+    float x[EPL];
+    S::load(q_t + ((long)gh * D + d0) * ES, x);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qbar[e] += x[e];
+  }
+  const float invG = 1.0f / (float)G;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qbar[e] *= invG;
+
+  float mrun = -INFINITY, lrun = 0.f, acck[EPL], accv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acck[e] = accv[e] = 0.f;
+  for (int c0 = 0; c0 < g; c0 += KPW) {
+    const int tau = c0 + ks;
+    const bool valid = tau < g;
+    float kx[EPL], vx[EPL];
+    if (valid) {
+      const int p = t - g + 1 + tau;
+      const char* kr;
+      const char* vr;
+      if (p == t) {
+        kr = k_new;
+        vr = v_new;
+      } else {
+        kr = ring_k + (long)(p % R) * D * ES;
+        vr = ring_v + (long)(p % R) * D * ES;
+      }
+      S::load(kr + d0 * ES, kx);
+      S::load(vr + d0 * ES, vx);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) kx[e] = vx[e] = 0.f;
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) part = fmaf(qbar[e], kx[e], part);
+#pragma unroll
+    for (int o = LPK / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    const float s = valid ? part * scale_log2 : -INFINITY;
+    const float mnew = fmaxf(mrun, s);
+    if (mnew != -INFINITY) {
+      const float alpha = exp2f(mrun - mnew);
+      const float pw = exp2f(s - mnew);
+      lrun = lrun * alpha + pw;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        acck[e] = fmaf(pw, kx[e], acck[e] * alpha);
+        accv[e] = fmaf(pw, vx[e], accv[e] * alpha);
+      }
+      mrun = mnew;
+    }
+  }
+#pragma unroll
+  for (int o = LPK; o < 64; o <<= 1) {
+    const float mo = __shfl_xor(mrun, o, 64);
+    const float lo = __shfl_xor(lrun, o, 64);
+    const float mnew = fmaxf(mrun, mo);
+    const float fa = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
+    const float fb = mo == -INFINITY ? 0.f : exp2f(mo - mnew);
+    lrun = lrun * fa + lo * fb;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float ko = __shfl_xor(acck[e], o, 64);
+      const float vo = __shfl_xor(accv[e], o, 64);
+      acck[e] = acck[e] * fa + ko * fb;
+      accv[e] = accv[e] * fa + vo * fb;
+    }
+    mrun = mnew;
+  }
+  if (ks == 0) {
+    const float inv = 1.0f / lrun;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      acck[e] *= inv;
+      accv[e] *= inv;
+    }
+    S::store(ck + d0 * ES, acck);
+    S::store(cv + d0 * ES, accv);
+  }
+}
+
+// Pass 1.  grid = (splits, Hq / GT, B); the block serves GT query heads.
+template <int DT, int D, int GT>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+    const void* __restrict__ q_t_, const void* __restrict__ k_t_, const void* __restrict__ v_t_,
+    void* __restrict__ ring_k_, void* __restrict__ ring_v_, int R, void* __restrict__ ck_,
+    void* __restrict__ cv_, int m_cap, const int32_t* __restrict__ pos, float* __restrict__ ws_m,
+    float* __restrict__ ws_l, float* __restrict__ ws_o, int Hq, int Hkv, int g, int w, int splits,
+    float scale_log2) {
+  typedef Slice<DT> S;
+  constexpr int ES = DT == 0 ? 4 : 2;
+  constexpr int EPL = S::N;
+  constexpr int LPK = D * ES / 16;   // lanes per key row
+  constexpr int KPW = 64 / LPK;      // key rows per wave load
+  constexpr int NW = kThreads / 64;
+
+  const int split = blockIdx.x;
+  const int hg = blockIdx.y;          // query-head group
+  const int b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int h0 = hg * GT;
+  const int hk = h0 / G;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ks = lane / LPK;
+  const int d0 = (lane % LPK) * EPL;
+  const int t = pos[b];
+  const long bhk = (long)b * Hkv + hk;
+  const long st_base = ((long)b * Hq + h0) * splits + split;  // partial state of head h0
+
+  if (!decode_valid(t, g, m_cap)) {
+    if (threadIdx.x < GT) ws_m[st_base + (long)threadIdx.x * splits] = NAN;
+    return;
+  }
+
+  const char* q_t = static_cast<const char*>(q_t_);
+  const char* k_new = static_cast<const char*>(k_t_) + bhk * D * ES;
+  const char* v_new = static_cast<const char*>(v_t_) + bhk * D * ES;
+  char* ring_k = static_cast<char*>(ring_k_) + bhk * R * D * ES;
+  char* ring_v = static_cast<char*>(ring_v_) + bhk * R * D * ES;
+  char* ck = static_cast<char*>(ck_) + bhk * m_cap * D * ES;
+  char* cv = static_cast<char*>(cv_) + bhk * m_cap * D * ES;
+
+  // Cache maintenance by one block per (b, kv head).
+  if (split == 0 && h0 % G == 0) {
+    if (wave == 0) {
+      // append k_t, v_t at slot t % R
+      const long slot = (long)(t % R) * D * ES;
+      for (int i = lane * 16; i < D * ES; i += 64 * 16) {
+        *reinterpret_cast<uint4*>(ring_k + slot + i) = *reinterpret_cast<const uint4*>(k_new + i);
+        *reinterpret_cast<uint4*>(ring_v + slot + i) = *reinterpret_cast<const uint4*>(v_new + i);
+      }
+    } else if (wave == 1 && (t + 1) % g == 0) {
+      const int jn = (t + 1) / g - 1;
+      pool_new_group<DT, D>(q_t + ((long)b * Hq + (long)hk * G) * D * ES, k_new, v_new, ring_k,
+                            ring_v, ck + (long)jn * D * ES, cv + (long)jn * D * ES, t, R, g, G,
+                            scale_log2);
+    }
+  }
+
+  const int nc = n_core(t, g, w);
+  const int lo = win_lo(t, w);
+  const int nvis = nc + (t - lo + 1);
+  const int chunk = (nvis + splits - 1) / splits;
+  const int f_begin = min(nvis, split * chunk);
+  const int f_end = min(nvis, f_begin + chunk);
+
+  float qs[GT][EPL];
+#pragma unroll
+  for (int i = 0; i < GT; ++i) {
+    S::load(q_t + (((long)b * Hq + h0 + i) * D + d0) * ES, qs[i]);
+  }
+  float mrun[GT], lrun[GT], acc[GT][EPL];
+#pragma unroll
+  for (int i = 0; i < GT; ++i) {
+    mrun[i] = -INFINITY;
+    lrun[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
+  }
+
+  // Each iteration: every lane group of every wave takes kBatch keys.
+  constexpr int kStep = NW * KPW * kBatch;
+  for (int f0 = f_begin; f0 < f_end; f0 += kStep) {
+    float kx[kBatch][EPL], vx[kBatch][EPL];
+    bool ok[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int f = f0 + (j * NW + wave) * KPW + ks;
+      ok[j] = f < f_end;
+      const char* kr = nullptr;
+      const char* vr = nullptr;
+      if (ok[j]) {
+        if (f < nc) {
+          kr = ck + (long)f * D * ES;
+          vr = cv + (long)f * D * ES;
+        } else {
+          const int p = lo + (f - nc);
+          if (p == t) {
+            kr = k_new;
+            vr = v_new;
+          } else {
+            kr = ring_k + (long)(p % R) * D * ES;
+            vr = ring_v + (long)(p % R) * D * ES;
+          }
+        }
+        S::load(kr + d0 * ES, kx[j]);
+        S::load(vr + d0 * ES, vx[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) kx[j][e] = vx[j][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GT; ++i) {
+      float s[kBatch];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) part = fmaf(qs[i][e], kx[j][e], part);
+#pragma unroll
+        for (int o = LPK / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        s[j] = ok[j] ? part * scale_log2 : -INFINITY;
+        mb = fmaxf(mb, s[j]);
+      }
+      const float mnew = fmaxf(mrun[i], mb);
+      if (mnew != -INFINITY) {
+        const float alpha = exp2f(mrun[i] - mnew);
+        lrun[i] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[i][e] *= alpha;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const float p = exp2f(s[j] - mnew);
+          lrun[i] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[i][e] = fmaf(p, vx[j][e], acc[i][e]);
+        }
+        mrun[i] = mnew;
+      }
+    }
+  }
+
+  // Merge lane groups within the wave, then the waves through LDS.
+  __shared__ float red_m[NW][GT];
+  __shared__ float red_l[NW][GT];
+  __shared__ float red_o[NW][GT][D];
+#pragma unroll
+  for (int i = 0; i < GT; ++i) {
+#pragma unroll
+    for (int o = LPK; o < 64; o <<= 1) {
+      const float mo = __shfl_xor(mrun[i], o, 64);
+      const float lo2 = __shfl_xor(lrun[i], o, 64);
+      const float mnew = fmaxf(mrun[i], mo);
+      const float fa = mrun[i] == -INFINITY ? 0.f : exp2f(mrun[i] - mnew);
+      const float fb = mo == -INFINITY ? 0.f : exp2f(mo - mnew);
+      lrun[i] = lrun[i] * fa + lo2 * fb;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float ao = __shfl_xor(acc[i][e], o, 64);
+        acc[i][e] = acc[i][e] * fa + ao * fb;
+      }
+      mrun[i] = mnew;
+    }
+    if (ks == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red_o[wave][i][d0 + e] = acc[i][e];
+      if (lane == 0) {
+        red_m[wave][i] = mrun[i];
+        red_l[wave][i] = lrun[i];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
+    const int i = idx / D, e = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, red_m[wv][i]);
+    float lsum = 0.f, osum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) {
+        const float f = red_m[wv][i] == -INFINITY ? 0.f : exp2f(red_m[wv][i] - M);
+        lsum += red_l[wv][i] * f;
+        osum += red_o[wv][i][e] * f;
+      }
+    }
+    const long st = st_base + (long)i * splits;
+    ws_o[st * D + e] = osum;
+    if (e == 0) {
+      ws_m[st] = M;
+      ws_l[st] = lsum;
+    }
+  }
+}
+
+// Pass 2.  One block of D threads per (b, query head).
+template <int OT, int D>
+__global__ __launch_bounds__(128) void decode_combine_kernel(
+    const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
+    void* __restrict__ out_, int32_t* __restrict__ pos, int advance_pos, int Hq, int splits) {
+  typedef Elem<OT> EO;
+  const long bh = blockIdx.x;
+  const int e = threadIdx.x;
+  const long st0 = bh * splits;
+  float M = -INFINITY;
+  bool bad = false;
+  for (int s = 0; s < splits; ++s) {
+    const float ms = ws_m[st0 + s];
+    bad |= isnan(ms);
+    M = fmaxf(M, ms);
+  }
+  float lsum = 0.f, osum = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float ms = ws_m[st0 + s];
+    if (ms == -INFINITY || isnan(ms)) continue;
+    const float f = exp2f(ms - M);
+    lsum += ws_l[st0 + s] * f;
+    osum += ws_o[(st0 + s) * D + e] * f;
+  }
+  const float r = bad ? NAN : osum / lsum;
+  if (e < D) EO::store(static_cast<typename EO::T*>(out_), bh * D + e, r);
+  if (advance_pos && e == 0 && bh % Hq == 0) pos[bh / Hq] += 1;
+}
+
+int pick_gt(int G) {
+  if (G % 8 == 0) return 8;
+  if (G % 4 == 0) return 4;
+  if (G % 2 == 0) return 2;
+  return 1;
+}
+
+template <int DT, int D, int GT>
+void launch_split(const void* q_t, const void* k_t, const void* v_t, void* ring_k, void* ring_v,
+                  int R, void* ck, void* cv, int m_cap, const int32_t* pos, float* ws_m,
+                  float* ws_l, float* ws_o, const Shape& sh, int splits, hipStream_t s) {
+  dim3 grid(splits, sh.Hq / GT, sh.B);
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  hipLaunchKernelGGL((decode_split_kernel<DT, D, GT>), grid, dim3(kThreads), 0, s, q_t, k_t, v_t,
+                     ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh.Hq, sh.Hkv, sh.g,
+                     sh.w, splits, scale_log2);
+}
+
+template <int DT, int D>
+void launch_split_g(int GT, const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                    void* ring_v, int R, void* ck, void* cv, int m_cap, const int32_t* pos,
+                    float* ws_m, float* ws_l, float* ws_o, const Shape& sh, int splits,
+                    hipStream_t s) {
+  switch (GT) {
+    case 8: launch_split<DT, D, 8>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, s); break;
+    case 4: launch_split<DT, D, 4>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, s); break;
+    case 2: launch_split<DT, D, 2>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, s); break;
+    default: launch_split<DT, D, 1>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, s); break;
+  }
+}
+
+}  // namespace
+
+DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int m_cap, int g, int w) {
+  (void)Hkv;
+  (void)g;
+  // Upper bound of visible keys: every core slot plus the window.
+  const long nvis_max = (long)m_cap + w;
+  long splits = (nvis_max + 255) / 256;
+  if (splits < 1) splits = 1;
+  if (splits > 64) splits = 64;
+  DecodePlan p;
+  p.splits = (int)splits;
+  p.ws_bytes = (size_t)B * Hq * splits * (size_t)(d + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                         void* ring_v, int R, void* ck, void* cv, int m_cap, int32_t* pos,
+                         int advance_pos, void* out, int out_dt, void* ws, const DecodePlan& plan,
+                         const Shape& sh, int dt, hipStream_t s) {
+  const int S = plan.splits;
+  float* ws_m = static_cast<float*>(ws);
+  float* ws_l = ws_m + (size_t)sh.B * sh.Hq * S;
+  float* ws_o = ws_l + (size_t)sh.B * sh.Hq * S;
+  const int GT = pick_gt(sh.G());
+  if (dt == 0) {
+    if (sh.d == 64) launch_split_g<0, 64>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
+    else launch_split_g<0, 128>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
+  } else {
+    if (sh.d == 64) launch_split_g<1, 64>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
+    else launch_split_g<1, 128>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)(sh.B * sh.Hq));
+  if (out_dt == 0) {
+    if (sh.d == 64) hipLaunchKernelGGL((decode_combine_kernel<0, 64>), grid, dim3(64), 0, s, ws_m, ws_l, ws_o, out, pos, advance_pos, sh.Hq, S);
+    else hipLaunchKernelGGL((decode_combine_kernel<0, 128>), grid, dim3(128), 0, s, ws_m, ws_l, ws_o, out, pos, advance_pos, sh.Hq, S);
+  } else {
+    if (sh.d == 64) hipLaunchKernelGGL((decode_combine_kernel<1, 64>), grid, dim3(64), 0, s, ws_m, ws_l, ws_o, out, pos, advance_pos, sh.Hq, S);
+    else hipLaunchKernelGGL((decode_combine_kernel<1, 128>), grid, dim3(128), 0, s, ws_m, ws_l, ws_o, out, pos, advance_pos, sh.Hq, S);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cca

@@ -1,0 +1,160 @@
+// Fused CCA prefill on the vector ALUs, fp32 arithmetic throughout.
+//
+// Computes, for every (b, h, t), one softmax over [cores 0..n_core(t)) ;
+// raw keys win_lo(t)..t] (digest at digest.lyk-ai.com/posts/2412.12465,
+// "Method", fusion formula).  This is the kernel for fp32 inputs and the
+// plain-arithmetic cross-check of the bf16 matrix-core kernel.
+//
+// A block owns 128 consecutive query rows of one query head; two threads share
+// a row, each holding half of the head dimension of q and of the output
+// accumulator.  The block walks the union of its rows' visible keys (cores
+// first, then the raw window) in tiles of 32 keys staged in LDS as fp32, and
+// applies each row's own visibility mask inside the tile.  Online softmax in
+// the log2 domain; one rescale per tile.
+#include "cca_device.hpp"
+#include "cca_internal.hpp"
+
+namespace cca {
+namespace {
+
+constexpr int kRows = 128;
+constexpr int kTile = 32;
+
+template <int DT, int OT, int D>
+__global__ __launch_bounds__(256) void prefill_valu_kernel(
+    const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
+    const void* __restrict__ ck_, const void* __restrict__ cv_, void* __restrict__ out_, int m_cap,
+    int Hq, int Hkv, int L, int g, int w, float scale_log2) {
+  typedef Elem<DT> E;
+  typedef typename E::T T;
+  constexpr int DH = D / 2;
+  __shared__ float sk[kTile][D + 1];
+  __shared__ float sv[kTile][D + 1];
+
+  const int tid = threadIdx.x;
+  const int half = tid & 1;
+  const int r = tid >> 1;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int hk = h / G;
+  const int t0 = blockIdx.x * kRows;
+  const int t_hi = min(L - 1, t0 + kRows - 1);
+  const int t = min(t0 + r, L - 1);  // rows past L compute a duplicate and store nothing
+
+  const T* q = static_cast<const T*>(q_);
+  const T* kk = static_cast<const T*>(k_);
+  const T* vv = static_cast<const T*>(v_);
+  const T* ck = static_cast<const T*>(ck_);
+  const T* cv = static_cast<const T*>(cv_);
+
+  float qr[DH], acc[DH];
+  const long qrow = ((long)(b * Hq + h) * L + t) * D + half * DH;
+#pragma unroll
+  for (int e = 0; e < DH; ++e) {
+    qr[e] = E::load(q, qrow + e);
+    acc[e] = 0.f;
+  }
+  const int my_nc = n_core(t, g, w);
+  const int my_lo = win_lo(t, w);
+
+  // Union of visible keys of this block's rows, as one flat index space:
+  // [0, nc_hi) are cores, [nc_hi, nc_hi + nraw) are raw positions raw_lo.. .
+  const int nc_hi = n_core(t_hi, g, w);
+  const int raw_lo = win_lo(t0, w);
+  const int nraw = t_hi - raw_lo + 1;
+  const int total = nc_hi + nraw;
+  const long kv_base = (long)(b * Hkv + hk);
+
+  float mrun = -INFINITY, lrun = 0.f;
+  for (int base = 0; base < total; base += kTile) {
+    __syncthreads();
+    for (int idx = tid; idx < kTile * D; idx += 256) {
+      const int i = idx / D, e = idx % D;
+      const int f = base + i;
+      float kx = 0.f, vx = 0.f;
+      if (f < nc_hi) {
+        const long off = (kv_base * m_cap + f) * D + e;
+        kx = E::load(ck, off);
+        vx = E::load(cv, off);
+      } else if (f < total) {
+        const long off = (kv_base * L + raw_lo + (f - nc_hi)) * D + e;
+        kx = E::load(kk, off);
+        vx = E::load(vv, off);
+      }
+      sk[i][e] = kx;
+      sv[i][e] = vx;
+    }
+    __syncthreads();
+    float s[kTile];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < DH; ++e) part = fmaf(qr[e], sk[i][half * DH + e], part);
+      part += __shfl_xor(part, 1, 64);
+      const int f = base + i;
+      bool vis;
+      if (f < nc_hi) {
+        vis = f < my_nc;
+      } else {
+        const int pos = raw_lo + (f - nc_hi);
+        vis = f < total && pos >= my_lo && pos <= t;
+      }
+      s[i] = vis ? part * scale_log2 : -INFINITY;
+      mt = fmaxf(mt, s[i]);
+    }
+    const float mnew = fmaxf(mrun, mt);
+    if (mnew == -INFINITY) continue;  // nothing visible to this row yet
+    const float alpha = exp2f(mrun - mnew);
+    lrun *= alpha;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) {
+      const float p = exp2f(s[i] - mnew);
+      lrun += p;
+#pragma unroll
+      for (int e = 0; e < DH; ++e) acc[e] = fmaf(p, sv[i][half * DH + e], acc[e]);
+    }
+    mrun = mnew;
+  }
+  if (t0 + r < L) {
+    typedef Elem<OT> EO;
+    typename EO::T* out = static_cast<typename EO::T*>(out_);
+    const float inv = 1.0f / lrun;
+    const long orow = ((long)(b * Hq + h) * L + t) * D + half * DH;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) EO::store(out, orow + e, acc[e] * inv);
+  }
+}
+
+template <int DT, int OT, int D>
+void launch_t(const void* q, const void* k, const void* v, const void* ck, const void* cv,
+              int m_cap, void* out, const Shape& sh, hipStream_t s) {
+  dim3 grid((sh.L + kRows - 1) / kRows, sh.Hq, sh.B);
+  const float scale_log2 = kLog2e / sqrtf((float)D);
+  hipLaunchKernelGGL((prefill_valu_kernel<DT, OT, D>), grid, dim3(256), 0, s, q, k, v, ck, cv, out,
+                     m_cap, sh.Hq, sh.Hkv, sh.L, sh.g, sh.w, scale_log2);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, const void* ck,
+                               const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
+                               int dt, hipStream_t s) {
+  if (dt == 0) {
+    if (sh.d == 64) launch_t<0, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, s);
+    else launch_t<0, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, s);
+  } else if (out_dt == 1) {
+    if (sh.d == 64) launch_t<1, 1, 64>(q, k, v, ck, cv, m_cap, out, sh, s);
+    else launch_t<1, 1, 128>(q, k, v, ck, cv, m_cap, out, sh, s);
+  } else {
+    if (sh.d == 64) launch_t<1, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, s);
+    else launch_t<1, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cca

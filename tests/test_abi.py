@@ -1,0 +1,115 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/cca.h declares, and rejects invalid arguments on the host before any
+HIP call (so no pointer below is ever dereferenced)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_long_context_cca_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "cca.h")
+FAKE = 0x10000       # 16-byte aligned, never dereferenced: every call below fails validation
+MIS = 0x10008        # misaligned
+OK, INV, UNS, CAP = (_lib.CCA_OK, _lib.CCA_ERR_INVALID_ARG, _lib.CCA_ERR_UNSUPPORTED,
+                     _lib.CCA_ERR_CAPACITY)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cca_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["cca_pool_core", "cca_attn_prefill", "cca_attn_decode", "cca_visibility_table",
+              "cca_decode_workspace_bytes", "cca_status_string", "cca_last_error", "cca_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(cca_lib):
+    for name in declared_functions():
+        assert hasattr(cca_lib, name), f"libcca.so does not export {name}"
+    assert sorted(_lib.EXPORTS) == declared_functions()
+
+
+def test_version_and_status_strings(cca_lib):
+    assert cca_lib.cca_version() >= 100
+    assert cca_lib.cca_status_string(OK) == b"CCA_OK"
+    assert cca_lib.cca_status_string(CAP) == b"CCA_ERR_CAPACITY"
+    assert cca_lib.cca_status_string(99) == b"CCA_ERR_UNKNOWN"
+
+
+P = ctypes.c_void_p
+
+
+def pool(lib, q=FAKE, k=FAKE, v=FAKE, ck=FAKE, cv=FAKE, m_cap=64, wts=None, B=1, Hq=4, Hkv=2, L=1024,
+         d=128, g=16, dt=1):
+    return lib.cca_pool_core(P(q), P(k), P(v), P(ck), P(cv), m_cap, P(wts), B, Hq, Hkv, L, d, g, dt, None)
+
+
+def prefill(lib, q=FAKE, k=FAKE, v=FAKE, ck=FAKE, cv=FAKE, m_cap=64, out=FAKE, out_dt=1, B=1, Hq=4,
+            Hkv=2, L=1024, d=128, g=16, w=64, dt=1, kernel=0):
+    return lib.cca_attn_prefill_ex(P(q), P(k), P(v), P(ck), P(cv), m_cap, P(out), out_dt, B, Hq, Hkv,
+                                   L, d, g, w, dt, kernel, None)
+
+
+def decode(lib, q=FAKE, kt=FAKE, vt=FAKE, rk=FAKE, rv=FAKE, R=1024, ck=FAKE, cv=FAKE, m_cap=4096,
+           pos=FAKE, adv=0, out=FAKE, out_dt=1, ws=FAKE, ws_bytes=1 << 30, B=2, Hq=8, Hkv=2, d=128,
+           g=16, w=1024, dt=1):
+    return lib.cca_attn_decode(P(q), P(kt), P(vt), P(rk), P(rv), R, P(ck), P(cv), m_cap, P(pos), adv,
+                               P(out), out_dt, P(ws), ws_bytes, B, Hq, Hkv, d, g, w, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(k=0), INV), (dict(v=MIS), INV), (dict(L=0), INV), (dict(g=0), INV),
+    (dict(B=0), INV), (dict(Hq=0), INV), (dict(dt=7), INV), (dict(d=96), UNS), (dict(Hq=3), UNS),
+    (dict(m_cap=63), CAP), (dict(ck=None), INV), (dict(wts=MIS), INV),
+    (dict(B=64, Hq=32, Hkv=32, L=131072, m_cap=8192), UNS),
+])
+def test_pool_validation(cca_lib, kw, code):
+    assert pool(cca_lib, **kw) == code
+    assert cca_lib.cca_last_error() != b""
+
+
+def test_pool_without_complete_group_is_a_no_op(cca_lib):
+    # L < g: nothing to pool, nothing enqueued, even with NULL core buffers
+    assert pool(cca_lib, L=15, ck=None, cv=None, m_cap=0) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), INV), (dict(w=0), INV), (dict(out_dt=5), INV), (dict(dt=0, out_dt=1), UNS),
+    (dict(kernel=3), INV), (dict(dt=0, out_dt=0, kernel=2), UNS), (dict(d=32), UNS),
+    (dict(Hkv=3), UNS), (dict(m_cap=10), CAP), (dict(cv=None), INV), (dict(q=MIS), INV),
+])
+def test_prefill_validation(cca_lib, kw, code):
+    assert prefill(cca_lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=1023), CAP), (dict(R=8, w=4, g=16), CAP), (dict(ws_bytes=16), CAP), (dict(pos=None), INV),
+    (dict(pos=FAKE + 2), INV), (dict(g=0), INV), (dict(w=0), INV), (dict(rk=None), INV),
+    (dict(out_dt=0, dt=0, d=80), UNS), (dict(Hq=6, Hkv=4), UNS), (dict(m_cap=-1), INV),
+    (dict(ck=None), INV), (dict(ws=None), INV),
+])
+def test_decode_validation(cca_lib, kw, code):
+    assert decode(cca_lib, **kw) == code
+
+
+def test_decode_workspace_size(cca_lib):
+    f = cca_lib.cca_decode_workspace_bytes
+    n = f(8, 32, 8, 128, 4112, 16, 1024)
+    assert n > 0 and n % 4 == 0
+    assert n == f(8, 32, 8, 128, 4112, 16, 1024)     # deterministic
+    assert f(16, 32, 8, 128, 4112, 16, 1024) == 2 * n  # linear in batch
+    assert f(0, 32, 8, 128, 4112, 16, 1024) == 0
+
+
+@pytest.mark.parametrize("args,code", [((0, 16, 4), INV), ((10, 0, 4), INV), ((10, 4, 0), INV)])
+def test_visibility_validation(cca_lib, args, code):
+    assert cca_lib.cca_visibility_table(*args, P(FAKE), P(FAKE), P(FAKE), None) == code
+    assert cca_lib.cca_visibility_table(10, 4, 4, P(None), P(FAKE), P(FAKE), None) == INV

@@ -1,0 +1,386 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 CPU oracle.
+
+Both sides take the same seeded input bits from ``cca_inputs``.  Bars:
+  * index tables: bit-exact;
+  * fp32 inputs: max abs error <= 1e-4; bf16 inputs: max abs error <= 2e-2
+    (outputs and caches rounded once to their storage dtype; bf16 P*V);
+  * pooled cores: fp32 1e-5 abs; bf16 within one half-ulp of the fp64 value
+    (2^-8 relative) plus 1e-6.
+Every case prints its name before it touches the GPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import cca_inputs
+import oracle.cca_oracle as orc
+import sparse_long_context_cca_amd as cca
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def f32np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float32).numpy()
+
+
+def err(gpu: torch.Tensor, ref: np.ndarray) -> float:
+    d = np.abs(host(gpu) - ref)
+    return float(d.max()) if d.size else 0.0
+
+
+def cfg_of(name, B, Hq, Hkv, L, d, g, w, dt, seed=90, spiky=False, steps=0, scale=1.0):
+    return cca_inputs.make_config(seed, name, B, Hq, Hkv, L, d, g, w, dt, scale=scale, spiky=spiky,
+                                  decode_steps=steps)
+
+
+def gpu_pool(q, k, v, g, m_cap=None, weights=False):
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    m = L // g
+    m_cap = max(m, 1) if m_cap is None else m_cap
+    ck = torch.full((B, Hkv, m_cap, d), float("nan"), dtype=q.dtype, device=DEV)
+    cv = torch.full_like(ck, float("nan"))
+    wt = torch.full((B, Hkv, max(m, 1), g), float("nan"), dtype=torch.float32, device=DEV) if weights else None
+    cca.cca_pool_core(q, k, v, ck, cv, g, weights=wt)
+    return ck, cv, wt
+
+
+# ------------------------------------------------------------- index tables
+
+
+@pytest.mark.parametrize("L,g,w", [(1, 1, 1), (37, 3, 5), (1024, 16, 64), (4099, 16, 1024),
+                                   (131072, 16, 1024), (300, 7, 300), (50, 64, 2), (65792, 16, 1024)])
+def test_visibility_tables_bit_exact(L, g, w):
+    say(f"visibility L={L} g={g} w={w}")
+    nc = torch.empty(L, dtype=torch.int32, device=DEV)
+    lo = torch.empty(L, dtype=torch.int32, device=DEV)
+    gl = torch.empty(max(L // g, 1), dtype=torch.int32, device=DEV)
+    cca.cca_visibility_table(L, g, w, nc, lo, gl)
+    torch.cuda.synchronize()
+    e_nc, e_lo, e_gl = orc.visibility(L, g, w)
+    assert np.array_equal(nc.cpu().numpy(), e_nc)
+    assert np.array_equal(lo.cpu().numpy(), e_lo)
+    if L // g:
+        assert np.array_equal(gl.cpu().numpy()[: L // g], e_gl)
+
+
+# ------------------------------------------------------------------ pooling
+
+POOL_CASES = [
+    # B, Hq, Hkv, L, d, g
+    (1, 1, 1, 16, 64, 16), (2, 4, 2, 37, 128, 3), (1, 8, 1, 300, 128, 16), (1, 2, 2, 97, 64, 1),
+    (1, 3, 1, 50, 128, 7), (2, 4, 4, 1024, 128, 16), (1, 6, 3, 129, 64, 40),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("case", POOL_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_pool_parity(dt, case):
+    B, Hq, Hkv, L, d, g = case
+    say(f"pool {dt} B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} g={g}")
+    cfg = cfg_of("pool", B, Hq, Hkv, L, d, g, 1, dt, seed=11 + L)
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    ck, cv, wt = gpu_pool(q.to(DEV), k.to(DEV), v.to(DEV), g, m_cap=L // g + 3, weights=True)
+    torch.cuda.synchronize()
+    CK, CV, A = orc.pool_core(f32np(q), f32np(k), f32np(v), g)
+    m = L // g
+    assert torch.isnan(ck[:, :, m:]).all(), "slots beyond L/g must be untouched"
+    if dt == "f32":
+        assert err(ck[:, :, :m], CK) <= 1e-5 and err(cv[:, :, :m], CV) <= 1e-5
+    else:
+        for got, ref in ((ck[:, :, :m], CK), (cv[:, :, :m], CV)):
+            bound = np.abs(ref) * 2.0 ** -8 * 1.01 + 1e-6
+            assert np.all(np.abs(host(got) - ref) <= bound)
+    assert err(wt[:, :, :m], A) <= 1e-5
+    assert float((wt[:, :, :m].sum(-1) - 1).abs().max()) <= 1e-5
+
+
+def test_pool_is_deterministic():
+    say("pool determinism")
+    cfg = cfg_of("det", 1, 8, 2, 4096, 128, 16, 1, "bf16", seed=5)
+    q, k, v = (x.to(DEV) for x in cca_inputs.prefill_inputs(cfg))
+    a = gpu_pool(q, k, v, 16)
+    b = gpu_pool(q, k, v, 16)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ prefill
+
+PREFILL_CASES = [
+    # B, Hq, Hkv, L, d, g, w
+    (1, 1, 1, 1024, 64, 16, 64),
+    (1, 4, 1, 300, 128, 16, 64),
+    (2, 8, 2, 517, 128, 16, 100),
+    (1, 2, 2, 250, 64, 3, 17),
+    (1, 8, 1, 200, 128, 1, 1),
+    (1, 2, 1, 129, 128, 16, 1000),
+    (1, 6, 3, 700, 64, 5, 33),
+    (1, 3, 1, 400, 128, 7, 40),
+    (1, 8, 1, 2000, 128, 16, 256),
+    (1, 1, 1, 1, 128, 16, 64),
+    (1, 4, 4, 4096, 128, 16, 1024),
+    (1, 16, 8, 3000, 128, 16, 512),
+    (2, 2, 1, 161, 128, 64, 2),
+]
+
+
+def run_prefill(cfg, kernel, out_dt):
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ck, cv, _ = gpu_pool(qd, kd, vd, cfg.g)
+    out = torch.full(q.shape, float("nan"), dtype=TORCH_DT[out_dt], device=DEV)
+    cca.cca_attn_prefill(qd, kd, vd, ck, cv, out, cfg.g, cfg.w, kernel=kernel)
+    torch.cuda.synchronize()
+    return (q, k, v), out
+
+
+def oracle_prefill(q, k, v, g, w):
+    Q, K, V = f32np(q), f32np(k), f32np(v)
+    CK, CV, _ = orc.pool_core(Q, K, V, g)
+    return orc.attn_prefill(Q, K, V, CK, CV, g, w)
+
+
+@pytest.mark.parametrize("kernel,dt,out_dt", [(1, "f32", "f32"), (1, "bf16", "bf16"), (2, "bf16", "bf16"),
+                                              (2, "bf16", "f32")])
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_prefill_parity(kernel, dt, out_dt, case):
+    B, Hq, Hkv, L, d, g, w = case
+    say(f"prefill kernel={kernel} {dt}->{out_dt} B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} g={g} w={w}")
+    cfg = cfg_of("prefill", B, Hq, Hkv, L, d, g, w, dt, seed=200 + L, scale=1.0 if dt == "bf16" else d ** -0.5)
+    (q, k, v), out = run_prefill(cfg, kernel, out_dt)
+    ref = oracle_prefill(q, k, v, g, w)
+    e = err(out, ref)
+    say(f"  max abs err {e:.3e}")
+    assert e <= TOL[dt]
+
+
+def test_prefill_c1_tiny_config():
+    cfg = cca_inputs.CONFIGS[1]
+    say(f"prefill config {cfg.name}")
+    (q, k, v), out = run_prefill(cfg, 0, "f32")
+    e = err(out, oracle_prefill(q, k, v, cfg.g, cfg.w))
+    say(f"  max abs err {e:.3e}")
+    assert e <= 1e-4
+
+
+def test_prefill_is_deterministic():
+    say("prefill determinism")
+    cfg = cfg_of("det", 1, 8, 2, 3000, 128, 16, 256, "bf16", seed=6)
+    _, a = run_prefill(cfg, 2, "bf16")
+    _, b = run_prefill(cfg, 2, "bf16")
+    assert torch.equal(a, b)
+
+
+def sample_rows(L, g, w, rng, n_random=40):
+    rows = {0, 1, L - 1, L - 2, L // 2}
+    for base in (w - 1, w, w + 1, w + g - 1, w + g, 2 * w + 3 * g - 1, L - w, L - w - 1):
+        for off in (0, g, 5 * g + 1):
+            rows.add(base + off)
+    rows.update(int(x) for x in rng.integers(0, L, n_random))
+    return sorted(r for r in rows if 0 <= r < L)
+
+
+@pytest.mark.parametrize("number", [2, 3, 4])
+def test_prefill_full_size_sampled(number):
+    """The three long-context workloads at full size, in the launch
+    configuration the benchmark times; sampled rows of selected heads."""
+    cfg = cca_inputs.CONFIGS[number]
+    say(f"prefill full-size config {cfg.name}: generating inputs")
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    say("  pool + prefill on GPU")
+    ck, cv, _ = gpu_pool(qd, kd, vd, cfg.g)
+    out = torch.empty_like(qd)
+    cca.cca_attn_prefill(qd, kd, vd, ck, cv, out, cfg.g, cfg.w)
+    torch.cuda.synchronize()
+    del qd, kd, vd
+    G = cfg.G
+    kv_heads = [0, cfg.Hkv - 1] if cfg.Hkv > 1 else [0]
+    rng = np.random.default_rng(number)
+    rows = sample_rows(cfg.L, cfg.g, cfg.w, rng)
+    worst = 0.0
+    for hk in kv_heads:
+        heads = list(range(hk * G, hk * G + G))
+        say(f"  oracle kv head {hk} (query heads {heads[0]}..{heads[-1]}), {len(rows)} rows")
+        K = f32np(k[:, hk : hk + 1])
+        V = f32np(v[:, hk : hk + 1])
+        Qh = f32np(q[:, heads[0] : heads[-1] + 1])
+        CK, CV, _ = orc.pool_core(Qh, K, V, cfg.g)
+        ref = orc.attn_rows(Qh, K, V, CK, CV, cfg.g, cfg.w, rows)
+        got = host(out[:, heads[0] : heads[-1] + 1, rows])
+        e = float(np.abs(got - ref).max())
+        worst = max(worst, e)
+        say(f"    max abs err {e:.3e}")
+    assert worst <= TOL[cfg.dtype]
+
+
+# ------------------------------------------------------------------- decode
+
+
+def decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed, advance=True):
+    """Decode `steps` tokens per sequence from caches built on the GPU (pool
+    kernel over the shared history + ring fill), checking every step."""
+    T = max(pos0) + steps
+    cfg = cfg_of("dec", B, Hq, Hkv, T, d, g, w, dt, seed=seed, scale=1.0 if dt == "bf16" else d ** -0.5)
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    Q, K, V = f32np(q), f32np(k), f32np(v)
+    CK, CV, _ = orc.pool_core(Q, K, V, g)
+    Lh = max(pos0)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ck = torch.zeros((B, Hkv, m_cap, d), dtype=q.dtype, device=DEV)
+    cv = torch.zeros_like(ck)
+    if Lh // g:
+        ck_h, cv_h, _ = gpu_pool(qd[:, :, :Lh], kd[:, :, :Lh], vd[:, :, :Lh], g)
+        n = min(m_cap, Lh // g)
+        ck[:, :, :n] = ck_h[:, :, :n]
+        cv[:, :, :n] = cv_h[:, :, :n]
+    rk = torch.zeros((B, Hkv, R, d), dtype=q.dtype, device=DEV)
+    rv = torch.zeros_like(rk)
+    for b in range(B):
+        for p in range(max(0, pos0[b] - R), pos0[b]):
+            rk[b, :, p % R] = kd[b, :, p]
+            rv[b, :, p % R] = vd[b, :, p]
+    pos = torch.tensor(pos0, dtype=torch.int32, device=DEV)
+    ws = torch.empty(cca.cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=q.dtype, device=DEV)
+    worst = 0.0
+    bidx = torch.arange(B, device=DEV)
+    for i in range(steps):
+        t = torch.tensor([p + i for p in pos0], device=DEV)
+        q_t = qd[bidx, :, t].contiguous()
+        k_t = kd[bidx, :, t].contiguous()
+        v_t = vd[bidx, :, t].contiguous()
+        if not advance:
+            pos.copy_(t.to(torch.int32))
+        cca.cca_attn_decode(q_t, k_t, v_t, rk, rv, ck, cv, pos, out, ws, g, w, advance_pos=advance)
+        torch.cuda.synchronize()
+        tt = np.array([p + i for p in pos0])
+        ref = orc.attn_decode(Q[np.arange(B), :, tt], K, V, CK, CV, tt, g, w)
+        worst = max(worst, err(out, ref))
+    final = pos.cpu().numpy()
+    expect_pos = np.array(pos0) + (steps if advance else steps - 1)
+    assert np.array_equal(final, expect_pos)
+    # caches: ring holds the last R positions; every completed group's core is pooled
+    for b in range(B):
+        tl = pos0[b] + steps
+        for p in range(max(0, tl - R), tl):
+            assert torch.equal(rk[b, :, p % R], kd[b, :, p]) and torch.equal(rv[b, :, p % R], vd[b, :, p])
+        nj = min(tl // g, m_cap)
+        if nj:
+            tol = 1e-5 if dt == "f32" else None
+            got, ref = host(ck[b, :, :nj]), CK[b, :, :nj]
+            if tol:
+                assert np.abs(got - ref).max() <= tol
+            else:
+                assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 * 1.01 + 1e-6)
+    return worst
+
+
+DECODE_CASES = [
+    # dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap
+    ("bf16", 128, 3, 8, 2, 4, 8, 8, [0, 5, 37], 40, 64),
+    ("f32", 64, 2, 4, 4, 16, 64, 64, [100, 300], 70, 64),
+    ("bf16", 128, 2, 4, 1, 16, 1024, 1024, [3000, 1100], 33, 256),
+    ("bf16", 64, 1, 2, 2, 3, 5, 7, [50], 30, 40),
+    ("f32", 128, 2, 16, 2, 16, 128, 160, [1, 700], 50, 64),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: f"{c[0]}-d{c[1]}-B{c[2]}-G{c[3] // c[4]}-g{c[5]}-w{c[6]}")
+def test_decode_parity(case):
+    dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap = case
+    say(f"decode {case}")
+    worst = decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed=300 + d + B)
+    say(f"  max abs err over steps {worst:.3e}")
+    assert worst <= TOL[dt]
+
+
+def test_decode_without_advancing_pos():
+    say("decode advance_pos=0")
+    worst = decode_run("bf16", 128, 2, 8, 2, 16, 64, 64, [80, 17], 20, 16, seed=7, advance=False)
+    assert worst <= TOL["bf16"]
+
+
+def test_decode_out_of_capacity_gives_nan_and_no_writes():
+    say("decode capacity overflow")
+    B, Hq, Hkv, d, g, w, R, m_cap = 2, 4, 2, 128, 4, 8, 8, 3
+    mk = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device=DEV)
+    q_t, k_t, v_t = mk(B, Hq, d) + 1, mk(B, Hkv, d) + 1, mk(B, Hkv, d) + 1
+    rk, rv, ck, cv = mk(B, Hkv, R, d), mk(B, Hkv, R, d), mk(B, Hkv, m_cap, d), mk(B, Hkv, m_cap, d)
+    pos = torch.tensor([10, 15], dtype=torch.int32, device=DEV)   # (15+1)/4 = 4 > m_cap = 3
+    ws = torch.empty(cca.cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w), dtype=torch.uint8, device=DEV)
+    out = mk(B, Hq, d)
+    cca.cca_attn_decode(q_t, k_t, v_t, rk, rv, ck, cv, pos, out, ws, g, w, advance_pos=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[0].float()).all() and torch.isnan(out[1].float()).all()
+    assert bool((rk[1] == 0).all()) and bool((ck[1] == 0).all())
+    assert pos.tolist() == [11, 16]
+
+
+def test_decode_c5_config():
+    """The decode workload: batch 8, 32/8 heads, 65536 cached tokens (cores from
+    the pool kernel, raw ring of 1024), 256 steps; every step, every (b, h)."""
+    cfg = cca_inputs.CONFIGS[5]
+    B, Hq, Hkv, d, g, w, L, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.g, cfg.w, cfg.L, cfg.decode_steps
+    R, m_cap = w, (L + S) // g
+    say(f"decode config {cfg.name}: generating inputs")
+    x = cca_inputs.decode_inputs(cfg)
+    K, V = f32np(x["k"]), f32np(x["v"])
+    n_end = L // g
+    q_last = np.zeros((B, Hq, (L + S) // g, d), dtype=np.float32)
+    q_last[:, :, :n_end] = f32np(x["q_ends"])
+    qs = f32np(x["q_steps"])
+    for i in range(S):            # groups completing during the steps are scored by the step query
+        if (L + i + 1) % g == 0:
+            q_last[:, :, (L + i + 1) // g - 1] = qs[:, :, i]
+    say("  oracle pooling")
+    CK, CV, _ = orc.pool_from_last(q_last, K, V, g)
+    say("  GPU caches")
+    kd, vd = x["k"].to(DEV), x["v"].to(DEV)
+    qfull = torch.zeros((B, Hq, L, d), dtype=torch.bfloat16, device=DEV)
+    qfull[:, :, g - 1 :: g] = x["q_ends"].to(DEV)
+    ck = torch.zeros((B, Hkv, m_cap, d), dtype=torch.bfloat16, device=DEV)
+    cv = torch.zeros_like(ck)
+    cca.cca_pool_core(qfull, kd[:, :, :L].contiguous(), vd[:, :, :L].contiguous(), ck, cv, g)
+    del qfull
+    rk = torch.empty((B, Hkv, R, d), dtype=torch.bfloat16, device=DEV)
+    rv = torch.empty_like(rk)
+    slots = torch.arange(L - R, L, device=DEV) % R
+    rk[:, :, slots] = kd[:, :, L - R : L]
+    rv[:, :, slots] = vd[:, :, L - R : L]
+    pos = torch.full((B,), L, dtype=torch.int32, device=DEV)
+    ws = torch.empty(cca.cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=DEV)
+    qsd = x["q_steps"].to(DEV)
+    outs = []
+    say(f"  {S} decode steps on GPU")
+    for i in range(S):
+        cca.cca_attn_decode(qsd[:, :, i].contiguous(), kd[:, :, L + i].contiguous(), vd[:, :, L + i].contiguous(),
+                            rk, rv, ck, cv, pos, out, ws, g, w, advance_pos=True)
+        outs.append(out.clone())
+    torch.cuda.synchronize()
+    say("  oracle steps")
+    worst = 0.0
+    for i in range(S):
+        t = np.full(B, L + i)
+        ref = orc.attn_decode(qs[:, :, i], K, V, CK, CV, t, g, w)
+        worst = max(worst, err(outs[i], ref))
+        if i % 64 == 0:
+            say(f"    step {i}: running max abs err {worst:.3e}")
+    say(f"  max abs err over {S} steps {worst:.3e}")
+    assert worst <= TOL["bf16"]
+    assert pos.tolist() == [L + S] * B
