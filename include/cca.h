@@ -38,7 +38,8 @@
  *     with a message available from cca_last_error() (per thread).
  *   - Input dtype `dt` applies to q, k, v and the core/ring caches.
  *     Supported: d in {64, 128}; dt in {CCA_F32, CCA_BF16}; out_dt in
- *     {dt, CCA_F32}.  Sizes must keep every buffer below 2^31 elements.
+ *     {dt, CCA_F32}.  Every buffer must hold at most 2^40 elements (offsets are
+ *     64-bit).
  *   - Rounding: accumulation is fp32; core K/V and outputs are rounded to their
  *     storage dtype once, to nearest even.  bf16 attention feeds the matrix
  *     cores bf16 operands (probabilities are rounded to bf16 before P*V).

@@ -37,7 +37,7 @@ cca_status from_hip(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-const long long kMaxElems = (1LL << 31) - 1;
+const long long kMaxElems = 1LL << 40;
 
 #define REQUIRE_PTR(p)                                                                  \
   do {                                                                                  \
@@ -67,7 +67,7 @@ cca_status check_out_dt(const char* fn, int out_dt, int dt) {
 
 cca_status check_sizes(const char* fn, long long a, long long b, long long c) {
   if (a > kMaxElems || b > kMaxElems || c > kMaxElems)
-    return fail(CCA_ERR_UNSUPPORTED, "%s: a buffer exceeds 2^31-1 elements", fn);
+    return fail(CCA_ERR_UNSUPPORTED, "%s: a buffer exceeds 2^40 elements", fn);
   return CCA_OK;
 }
 

@@ -69,7 +69,7 @@ def decode(lib, q=FAKE, kt=FAKE, vt=FAKE, rk=FAKE, rv=FAKE, R=1024, ck=FAKE, cv=
     (dict(q=None), INV), (dict(k=0), INV), (dict(v=MIS), INV), (dict(L=0), INV), (dict(g=0), INV),
     (dict(B=0), INV), (dict(Hq=0), INV), (dict(dt=7), INV), (dict(d=96), UNS), (dict(Hq=3), UNS),
     (dict(m_cap=63), CAP), (dict(ck=None), INV), (dict(wts=MIS), INV),
-    (dict(B=64, Hq=32, Hkv=32, L=131072, m_cap=8192), UNS),
+    (dict(B=1 << 16, Hq=1 << 10, Hkv=1 << 10, L=1 << 12, m_cap=256), UNS),
 ])
 def test_pool_validation(cca_lib, kw, code):
     assert pool(cca_lib, **kw) == code

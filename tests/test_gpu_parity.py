@@ -244,7 +244,8 @@ def decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed, advance=Tru
     ck = torch.zeros((B, Hkv, m_cap, d), dtype=q.dtype, device=DEV)
     cv = torch.zeros_like(ck)
     if Lh // g:
-        ck_h, cv_h, _ = gpu_pool(qd[:, :, :Lh], kd[:, :, :Lh], vd[:, :, :Lh], g)
+        ck_h, cv_h, _ = gpu_pool(qd[:, :, :Lh].contiguous(), kd[:, :, :Lh].contiguous(),
+                                 vd[:, :, :Lh].contiguous(), g)
         n = min(m_cap, Lh // g)
         ck[:, :, :n] = ck_h[:, :, :n]
         cv[:, :, :n] = cv_h[:, :, :n]
