@@ -363,32 +363,56 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
 }
 
-// Pass 2.  One block of D threads per (b, query head).
+// Pass 2.  One block of D threads per (b, query head).  The split states are
+// staged in LDS first so that the weighted sum issues independent loads.
+constexpr int kMaxSplits = 128;
+
 template <int OT, int D>
 __global__ __launch_bounds__(128) void decode_combine_kernel(
     const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
     void* __restrict__ out_, int32_t* __restrict__ pos, int advance_pos, int Hq, int splits) {
   typedef Elem<OT> EO;
+  __shared__ float sm[kMaxSplits];
+  __shared__ float sl[kMaxSplits];
+  __shared__ float red[2];
   const long bh = blockIdx.x;
   const int e = threadIdx.x;
   const long st0 = bh * splits;
-  float M = -INFINITY;
-  bool bad = false;
-  for (int s = 0; s < splits; ++s) {
-    const float ms = ws_m[st0 + s];
-    bad |= isnan(ms);
-    M = fmaxf(M, ms);
+  for (int s = e; s < splits; s += D) {
+    sm[s] = ws_m[st0 + s];
+    sl[s] = ws_l[st0 + s];
   }
+  __syncthreads();
+  if (e < 64) {
+    float M = -INFINITY;
+    float bad = 0.f;
+    for (int s = e; s < splits; s += 64) {
+      M = fmaxf(M, sm[s]);
+      bad += isnan(sm[s]) ? 1.f : 0.f;
+    }
+    M = wave_max(M);
+    bad = wave_sum(bad);
+    if (e == 0) {
+      red[0] = M;
+      red[1] = bad;
+    }
+  }
+  __syncthreads();
+  const float M = red[0];
+  for (int s = e; s < splits; s += D) {
+    const float ms = sm[s];
+    sm[s] = (ms == -INFINITY || isnan(ms)) ? 0.f : exp2f(ms - M);  // weight of split s
+  }
+  __syncthreads();
   float lsum = 0.f, osum = 0.f;
+#pragma unroll 8
   for (int s = 0; s < splits; ++s) {
-    const float ms = ws_m[st0 + s];
-    if (ms == -INFINITY || isnan(ms)) continue;
-    const float f = exp2f(ms - M);
-    lsum += ws_l[st0 + s] * f;
-    osum += ws_o[(st0 + s) * D + e] * f;
+    const float f = sm[s];
+    lsum = fmaf(sl[s], f, lsum);
+    osum = fmaf(ws_o[(st0 + s) * D + e], f, osum);
   }
-  const float r = bad ? NAN : osum / lsum;
-  if (e < D) EO::store(static_cast<typename EO::T*>(out_), bh * D + e, r);
+  const float r = red[1] != 0.f ? NAN : osum / lsum;
+  EO::store(static_cast<typename EO::T*>(out_), bh * D + e, r);
   if (advance_pos && e == 0 && bh % Hq == 0) pos[bh / Hq] += 1;
 }
 
@@ -430,9 +454,9 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int m_cap, int g, int w) {
   (void)g;
   // Upper bound of visible keys: every core slot plus the window.
   const long nvis_max = (long)m_cap + w;
-  long splits = (nvis_max + 255) / 256;
+  long splits = (nvis_max + 127) / 128;
   if (splits < 1) splits = 1;
-  if (splits > 64) splits = 64;
+  if (splits > kMaxSplits) splits = kMaxSplits;
   DecodePlan p;
   p.splits = (int)splits;
   p.ws_bytes = (size_t)B * Hq * splits * (size_t)(d + 2) * sizeof(float);

@@ -41,6 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kThreads = 256;
 constexpr int kBK = 64;       // keys per tile
 constexpr int kVRow = 144;    // bytes per transposed-V row: 64 keys + 16 pad
+constexpr float kLazyLog2 = 8.0f;  // rescale threshold of the running max, log2 units
 
 struct PrefillParams {
   const uint16_t* q;
@@ -70,7 +71,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 }
 
 template <int D, int OT>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams P) {
+// Two waves per SIMD (the accumulators stay in arch VGPRs, 256 per wave) so
+// that one wave's softmax overlaps the other's matrix ops.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(PrefillParams P) {
   constexpr int KS = D / 16;            // k-steps of Q.K^T
   constexpr int DB = D / 32;            // 32-wide dim blocks of the output
   constexpr int KRow = D * 2 + 16;      // bytes per K row in LDS (padded)
@@ -264,10 +268,22 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams P)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
       mt = pair_max(mt);
+      // Lazy rescale: the reference max m only moves when the row max grows by
+      // more than kLazyLog2 (log2 units), so probabilities stay <= 2^kLazyLog2
+      // and the accumulator rescale is skipped on almost every tile.  The
+      // final normalisation divides by a sum taken against the same m.
       const float mnew = fmaxf(m, mt);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f((m - muse) * c);
-      const float mc = muse * c;
+      const bool grow = (mnew - m) * c > kLazyLog2;  // false while both are -inf
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m - mnew) * c) : 1.0f;
+        m = grow ? mnew : m;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      const float mc = (m == -INFINITY ? 0.f : m) * c;
       float lsum = 0.f;
       bf16x8 pb[4];
 #pragma unroll
@@ -278,12 +294,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams P)
           lsum += p;
           pb[2 * kb + (r >> 3)][r & 7] = static_cast<__bf16>(p);
         }
-      l = l * alpha + lsum;
-      m = mnew;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l += lsum;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
