@@ -185,6 +185,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="first run one device-to-device copy of this many bytes (a counter "
+                         "calibration reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no sharding or collectives); "
@@ -194,6 +197,13 @@ def main():
     import sparse_long_context_cca_amd as cca
     cca.load()
     dev = "cuda:0"
+    if args.copy_bytes:
+        n = args.copy_bytes // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = cca_inputs.CONFIGS[4]
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
     q, k, v = cca_inputs.prefill_inputs(cfg)

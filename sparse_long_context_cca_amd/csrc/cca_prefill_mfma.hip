@@ -89,7 +89,9 @@ void prefill_mfma_kernel(PrefillParams P) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave index as a scalar, so that every per-wave quantity below (rows,
+  // tile visibility) is known to be uniform and branches on it stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31;
   const int hh = lane >> 5;
 
@@ -150,33 +152,39 @@ void prefill_mfma_kernel(PrefillParams P) {
   }
 
   // ---- tile loaders (global -> registers -> LDS)
-  uint4 kreg[NPK];
-  uint4 vreg[4];
+  // Buffer loads: the resource of each tile starts at the tile's first key and
+  // spans only its valid keys, so rows past the end (beyond the last visible
+  // core, or past the last row of the workgroup) read as zero in hardware.
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 kreg[NPK];
+  u32x4 vreg[4];
   const int k_oct = tid % LPR;
   const int k_row0 = tid / LPR;
   const int v_oct = tid / 16;   // dim octet
   const int v_quad = tid % 16;  // key quad
   const bool v_act = tid < NVQ;
+  int koff[NPK], voff[4];
+#pragma unroll
+  for (int i = 0; i < NPK; ++i) koff[i] = ((k_row0 + i * KPP) * D + 8 * k_oct) * 2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = ((4 * v_quad + i) * D + 8 * v_oct) * 2;
 
   auto load_tile = [&](int it) {
     const bool core = it < n_ct;
     const int base = core ? it * kBK : r0 + (it - n_ct) * kBK;
-    const int lim = core ? nc_hi : P_hi + 1;  // keys base+kk valid while < lim
-    const uint16_t* ksrc = core ? ckbase : kbase;
-    const uint16_t* vsrc = core ? cvbase : vbase;
+    const int lim = core ? nc_hi : P_hi + 1;  // keys < lim are valid
+    const int nvalid = min(kBK, lim - base);
+    const uint16_t* ks = (core ? ckbase : kbase) + (long)base * D;
+    const uint16_t* vs = (core ? cvbase : vbase) + (long)base * D;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ks), 0, nvalid * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vs), 0, nvalid * D * 2, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) {
-      const int key = base + k_row0 + i * KPP;
-      kreg[i] = key < lim ? *reinterpret_cast<const uint4*>(ksrc + (long)key * D + 8 * k_oct)
-                          : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < NPK; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0);
     if (v_act) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = base + 4 * v_quad + i;
-        vreg[i] = key < lim ? *reinterpret_cast<const uint4*>(vsrc + (long)key * D + 8 * v_oct)
-                            : make_uint4(0, 0, 0, 0);
-      }
+      for (int i = 0; i < 4; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, 0);
     }
   };
   auto store_tile = [&](int stage) {
@@ -184,26 +192,18 @@ void prefill_mfma_kernel(PrefillParams P) {
     char* vt = kt + KBytes;
 #pragma unroll
     for (int i = 0; i < NPK; ++i)
-      *reinterpret_cast<uint4*>(kt + (k_row0 + i * KPP) * KRow + 16 * k_oct) = kreg[i];
+      *reinterpret_cast<u32x4*>(kt + (k_row0 + i * KPP) * KRow + 16 * k_oct) = kreg[i];
     if (v_act) {
-      // keys 4q..4q+3 land at permuted positions kpos0..kpos0+3 (bits 2,3 of the key swapped)
+      // keys 4q..4q+3 land at permuted positions kpos0..kpos0+3 (bits 2,3 of the key swapped);
+      // dim 8*v_oct+i of the four keys becomes one 8-byte row segment of V^T.
       const int q = v_quad;
       const int kpos0 = 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
-      const uint32_t* r0w = reinterpret_cast<const uint32_t*>(&vreg[0]);
-      const uint32_t* r1w = reinterpret_cast<const uint32_t*>(&vreg[1]);
-      const uint32_t* r2w = reinterpret_cast<const uint32_t*>(&vreg[2]);
-      const uint32_t* r3w = reinterpret_cast<const uint32_t*>(&vreg[3]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int dw = i >> 1;
-        uint32_t lo, hi;
-        if ((i & 1) == 0) {
-          lo = (r0w[dw] & 0xffffu) | (r1w[dw] << 16);
-          hi = (r2w[dw] & 0xffffu) | (r3w[dw] << 16);
-        } else {
-          lo = (r0w[dw] >> 16) | (r1w[dw] & 0xffff0000u);
-          hi = (r2w[dw] >> 16) | (r3w[dw] & 0xffff0000u);
-        }
+        const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo = __builtin_amdgcn_perm(vreg[1][dw], vreg[0][dw], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(vreg[3][dw], vreg[2][dw], sel);
         *reinterpret_cast<uint2*>(vt + (8 * v_oct + i) * kVRow + 2 * kpos0) = make_uint2(lo, hi);
       }
     }
@@ -216,6 +216,8 @@ void prefill_mfma_kernel(PrefillParams P) {
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m = -INFINITY, l = 0.f;
   const float c = P.c;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   load_tile(0);
   store_tile(0);
@@ -252,13 +254,18 @@ void prefill_mfma_kernel(PrefillParams P) {
         }
       }
       if (!full) {
+        // (the empty asm keeps this a real branch: masks are needed on edge tiles only)
+        asm volatile("" ::: "memory");
+        // key kk of the tile is visible to this lane's row iff lo_rel <= kk <= hi_rel
+        const int lo_rel = core ? 0 : my_lo - base;
+        const int hi_rel = core ? my_nc - 1 - base : t - base;
+        const unsigned span = (unsigned)(hi_rel - lo_rel);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const int key = base + kk;
-            const bool vis = core ? key < my_nc : (key >= my_lo && key <= t);
+            const bool vis = hi_rel >= lo_rel && (unsigned)(kk - lo_rel) <= span;
             s[kb][r] = vis ? s[kb][r] : -INFINITY;
           }
       }
@@ -284,17 +291,21 @@ void prefill_mfma_kernel(PrefillParams P) {
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
       const float mc = (m == -INFINITY ? 0.f : m) * c;
-      float lsum = 0.f;
       bf16x8 pb[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
-          lsum += p;
-          pb[2 * kb + (r >> 3)][r & 7] = static_cast<__bf16>(p);
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -mc));
+          bf16x2 pk;
+          pk[0] = static_cast<__bf16>(p0);
+          pk[1] = static_cast<__bf16>(p1);
+          // row sum of the rounded probabilities actually fed to P.V
+          l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l, false);
+          pb[2 * kb + (r >> 3)][r & 7] = pk[0];
+          pb[2 * kb + (r >> 3)][(r & 7) + 1] = pk[1];
         }
-      l += lsum;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
