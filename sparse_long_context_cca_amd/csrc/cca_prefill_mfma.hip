@@ -123,18 +123,22 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int t = min(t_raw, L - 1);
   const int my_nc = n_core(t, g, w);
   const int my_lo = win_lo(t, w);
-  const int w_lo = min(p0, L - 1);
-  const int w_hi = min(p0 + 31, L - 1);
-  const int wnc_lo = n_core(w_lo, g, w), wnc_hi = n_core(w_hi, g, w);
-  const int wlo_lo = win_lo(w_lo, w), wlo_hi = win_lo(w_hi, w);
+  // Per-wave and per-workgroup bounds are uniform; readfirstlane keeps them in
+  // scalar registers (the integer divisions inside n_core run on the vector
+  // ALUs), so that the tile branches below stay scalar branches.
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  const int w_lo = uni(min(p0, L - 1));
+  const int w_hi = uni(min(p0 + 31, L - 1));
+  const int wnc_lo = uni(n_core(w_lo, g, w)), wnc_hi = uni(n_core(w_hi, g, w));
+  const int wlo_lo = uni(win_lo(w_lo, w)), wlo_hi = uni(win_lo(w_hi, w));
 
   // ---- workgroup key range
-  const int nc_hi = n_core(P_hi, g, w);
+  const int nc_hi = uni(n_core(P_hi, g, w));
   const int n_ct = (nc_hi + kBK - 1) / kBK;
   const int raw_lo = win_lo(P_lo, w);
   const int r0 = raw_lo & ~(kBK - 1);
   const int n_rt = (P_hi - r0) / kBK + 1;
-  const int n_tiles = n_ct + n_rt;
+  const int n_tiles = uni(n_ct + n_rt);
 
   const long kvrow = (long)kvp;
   const uint16_t* kbase = P.k + kvrow * L * D;
@@ -162,40 +166,49 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int k_row0 = tid / LPR;
   const int v_oct = tid / 16;   // dim octet
   const int v_quad = tid % 16;  // key quad
-  const bool v_act = tid < NVQ;
+  const bool v_act = NVQ >= kThreads || tid < NVQ;  // all threads when D = 128
   int koff[NPK], voff[4];
 #pragma unroll
   for (int i = 0; i < NPK; ++i) koff[i] = ((k_row0 + i * KPP) * D + 8 * k_oct) * 2;
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = ((4 * v_quad + i) * D + 8 * v_oct) * 2;
 
-  auto load_tile = [&](int it) {
-    const bool core = it < n_ct;
-    const int base = core ? it * kBK : r0 + (it - n_ct) * kBK;
+  auto tile_core = [&](int it) { return it < n_ct; };
+  auto tile_base = [&](int it) { return it < n_ct ? it * kBK : r0 + (it - n_ct) * kBK; };
+  auto rsrc = [&](int it, bool values) {
+    const bool core = tile_core(it);
+    const int base = tile_base(it);
     const int lim = core ? nc_hi : P_hi + 1;  // keys < lim are valid
-    const int nvalid = min(kBK, lim - base);
-    const uint16_t* ks = (core ? ckbase : kbase) + (long)base * D;
-    const uint16_t* vs = (core ? cvbase : vbase) + (long)base * D;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(ks), 0, nvalid * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vs), 0, nvalid * D * 2, 0x00020000);
+    const int nvalid = max(0, min(kBK, lim - base));  // 0 past the last tile
+    const uint16_t* src = (core ? (values ? cvbase : ckbase) : (values ? vbase : kbase)) + (long)base * D;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, nvalid * D * 2, 0x00020000);
+  };
+  auto load_k = [&](int it) {
+    const __amdgpu_buffer_rsrc_t r = rsrc(it, false);
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[i], 0, 0);
+    for (int i = 0; i < NPK; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff[i], 0, 0);
+  };
+  auto load_v = [&](int it) {
     if (v_act) {
+      const __amdgpu_buffer_rsrc_t r = rsrc(it, true);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[i], 0, 0);
+      for (int i = 0; i < 4; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i], 0, 0);
     }
   };
-  auto store_tile = [&](int stage) {
-    char* kt = lds + stage * Stage;
-    char* vt = kt + KBytes;
+  // LDS: [K buffer 0 | K buffer 1 | V^T buffer 0 | V^T buffer 1]
+  auto kbuf = [&](int i) { return lds + i * KBytes; };
+  auto vbuf = [&](int i) { return lds + 2 * KBytes + i * VBytes; };
+  auto store_k = [&](int buf) {
+    char* kt = kbuf(buf);
 #pragma unroll
     for (int i = 0; i < NPK; ++i)
       *reinterpret_cast<u32x4*>(kt + (k_row0 + i * KPP) * KRow + 16 * k_oct) = kreg[i];
+  };
+  auto store_v = [&](int buf) {
     if (v_act) {
       // keys 4q..4q+3 land at permuted positions kpos0..kpos0+3 (bits 2,3 of the key swapped);
       // dim 8*v_oct+i of the four keys becomes one 8-byte row segment of V^T.
+      char* vt = vbuf(buf);
       const int q = v_quad;
       const int kpos0 = 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
 #pragma unroll
@@ -208,6 +221,12 @@ void prefill_mfma_kernel(PrefillParams P) {
       }
     }
   };
+  // Does tile it need a mask for this wave's rows?  (wave-uniform)  A tile
+  // none of the wave's rows can see is simply fully masked.
+  auto tile_full = [&](int it) {
+    const int base = tile_base(it);
+    return tile_core(it) ? base + kBK <= wnc_lo : (base >= wlo_hi && base + kBK - 1 <= w_lo);
+  };
 
   f32x16 o[DB];
 #pragma unroll
@@ -219,105 +238,145 @@ void prefill_mfma_kernel(PrefillParams P) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  load_tile(0);
-  store_tile(0);
+  // prologue: K(0) staged; V buffer 1 (read as "tile -1") cleared
+  load_k(0);
+  store_k(0);
+  for (int i = tid; i < VBytes / 16; i += kThreads)
+    *reinterpret_cast<u32x4*>(vbuf(1) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
+  // probabilities of the previous tile (zeros before the first), bf16 B operands
+  bf16x8 pr[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[cc][e] = static_cast<__bf16>(0.0f);
 
+  // Iteration it: LDS holds K(it) and V(it-1); the loads of K(it+1) and V(it)
+  // are in flight and stored at its end.  S = Q.K^T(it) on the matrix cores;
+  // then tile it's softmax on the vector ALUs while the matrix cores run P.V
+  // of tile it-1.  Chunk cc of pr is consumed by that P.V just before tile
+  // it's chunk cc overwrites it.  The rescale a new max demands (alpha) is
+  // applied to the accumulators at the top of the next iteration, i.e. after
+  // the P.V of tile it-1 and before that of tile it.  The loop body is kept
+  // free of branches between the max and the barrier so that the P.V MFMAs
+  // and the exponentials share one scheduling region.
+  bool grow_pending = false;
+  float alpha_pending = 1.0f;
   for (int it = 0; it < n_tiles; ++it) {
-    const int stage = it & 1;
-    if (it + 1 < n_tiles) load_tile(it + 1);
-
-    const bool core = it < n_ct;
-    const int base = core ? it * kBK : r0 + (it - n_ct) * kBK;
-    // visibility of this tile for the wave's rows (wave-uniform)
-    bool skip, full;
-    if (core) {
-      skip = base >= wnc_hi;
-      full = base + kBK <= wnc_lo;
-    } else {
-      skip = base > w_hi || base + kBK - 1 < wlo_lo;
-      full = base >= wlo_hi && base + kBK - 1 <= w_lo;
+    load_k(it + 1);  // empty past the last tile
+    load_v(it);
+    if (grow_pending) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
     }
-    if (!skip) {
-      const char* kt = lds + stage * Stage;
-      const char* vt = kt + KBytes;
-      f32x16 s[2];
+    const char* kt = kbuf(it & 1);
+    const char* vt_prev = vbuf((it + 1) & 1);
+    f32x16 sx[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sx[kb][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(kt + (32 * kb + j) * KRow + (16 * ks + 8 * hh) * 2);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + (32 * kb + j) * KRow + (16 * ks + 8 * hh) * 2);
+        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sx[kb], 0, 0, 0);
       }
-      if (!full) {
-        // (the empty asm keeps this a real branch: masks are needed on edge tiles only)
-        asm volatile("" ::: "memory");
-        // key kk of the tile is visible to this lane's row iff lo_rel <= kk <= hi_rel
-        const int lo_rel = core ? 0 : my_lo - base;
-        const int hi_rel = core ? my_nc - 1 - base : t - base;
-        const unsigned span = (unsigned)(hi_rel - lo_rel);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool vis = hi_rel >= lo_rel && (unsigned)(kk - lo_rel) <= span;
-            s[kb][r] = vis ? s[kb][r] : -INFINITY;
-          }
-      }
-      float mt = -INFINITY;
+    }
+    if (!tile_full(it)) {
+      // key kk of the tile is visible to this lane's row iff lo_rel <= kk <= hi_rel
+      asm volatile("" ::: "memory");  // keeps this a real (scalar) branch
+      const int base = tile_base(it);
+      const bool core = tile_core(it);
+      const int lo_rel = core ? 0 : my_lo - base;
+      const int hi_rel = core ? my_nc - 1 - base : t - base;
+      const unsigned span = (unsigned)(hi_rel - lo_rel);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-      mt = pair_max(mt);
-      // Lazy rescale: the reference max m only moves when the row max grows by
-      // more than kLazyLog2 (log2 units), so probabilities stay <= 2^kLazyLog2
-      // and the accumulator rescale is skipped on almost every tile.  The
-      // final normalisation divides by a sum taken against the same m.
-      const float mnew = fmaxf(m, mt);
-      const bool grow = (mnew - m) * c > kLazyLog2;  // false while both are -inf
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f((m - mnew) * c) : 1.0f;
-        m = grow ? mnew : m;
-        l *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool vis = hi_rel >= lo_rel && (unsigned)(kk - lo_rel) <= span;
+          sx[kb][r] = vis ? sx[kb][r] : -INFINITY;
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sx[kb][r]);
+    mt = pair_max(mt);
+    // Lazy rescale: the reference max m only moves when the row max grows by
+    // more than kLazyLog2 (log2 units), so probabilities stay <= 2^kLazyLog2
+    // and the accumulator rescale is skipped on almost every tile.  The final
+    // normalisation divides by a sum taken against the same m.
+    const float mnew = fmaxf(m, mt);
+    const bool grow = (mnew - m) * c > kLazyLog2;  // false while both are -inf
+    const float ex = __builtin_amdgcn_exp2f((m - mnew) * c);  // NaN while both are -inf; unused then
+    const float alpha = grow ? ex : 1.0f;
+    m = grow ? mnew : m;
+    l *= alpha;
+    const float mc = (m == -INFINITY ? 0.f : m) * c;
+    // P.V of tile it-1 interleaved by hand with tile it's exponentials: after
+    // each MFMA (32 cycles on the matrix core) come the two probabilities it
+    // can hide (2 fma, 2 exp, 1 convert, 1 dot2).  sched_barrier freezes that
+    // order; the V^T fragments of the next chunk are read one chunk ahead.
+    static_assert(DB == 2 || DB == 4, "head dim 64 or 128");
+    constexpr int PPM = 8 / DB;  // probabilities per MFMA slot
+    bf16x8 vfr[2][DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vfr[0][db] = *reinterpret_cast<const bf16x8*>(vt_prev + (32 * db + j) * kVRow + (8 * hh) * 2);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      if (cc + 1 < 4) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          vfr[(cc + 1) & 1][db] = *reinterpret_cast<const bf16x8*>(
+              vt_prev + (32 * db + j) * kVRow + (16 * (cc + 1) + 8 * hh) * 2);
       }
-      const float mc = (m == -INFINITY ? 0.f : m) * c;
-      bf16x8 pb[4];
+      bf16x8 pnew;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int db = 0; db < DB; ++db) {
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[cc & 1][db], pr[cc], o[db], 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -mc));
+        for (int e = db * PPM; e < db * PPM + PPM; e += 2) {
+          const int r = (cc & 1) * 8 + e;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r + 1], c, -mc));
           bf16x2 pk;
           pk[0] = static_cast<__bf16>(p0);
           pk[1] = static_cast<__bf16>(p1);
           // row sum of the rounded probabilities actually fed to P.V
           l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l, false);
-          pb[2 * kb + (r >> 3)][r & 7] = pk[0];
-          pb[2 * kb + (r >> 3)][(r & 7) + 1] = pk[1];
+          pnew[e] = pk[0];
+          pnew[e + 1] = pk[1];
         }
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(vt + (32 * db + j) * kVRow + (16 * cc + 8 * hh) * 2);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], o[db], 0, 0, 0);
-        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      pr[cc] = pnew;
     }
-    if (it + 1 < n_tiles) store_tile(stage ^ 1);
+    grow_pending = __builtin_amdgcn_ballot_w64(grow) != 0;
+    alpha_pending = alpha;
+    store_k((it + 1) & 1);
+    store_v(it & 1);
     __syncthreads();
   }
+  if (grow_pending) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
+  }
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const char* vt = vbuf((n_tiles - 1) & 1);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + j) * kVRow + (16 * cc + 8 * hh) * 2);
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pr[cc], o[db], 0, 0, 0);
+    }
 
   // ---- normalise and store: lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
   const float ltot = pair_sum(l);
