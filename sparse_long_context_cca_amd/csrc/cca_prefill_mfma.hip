@@ -38,7 +38,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
 constexpr int kBK = 64;       // keys per tile
 constexpr int kVRow = 144;    // bytes per transposed-V row: 64 keys + 16 pad
 constexpr float kLazyLog2 = 8.0f;  // rescale threshold of the running max, log2 units
@@ -70,11 +69,12 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, int OT>
 // Two waves per SIMD (the accumulators stay in arch VGPRs, 256 per wave) so
 // that one wave's softmax overlaps the other's matrix ops.
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int OT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillParams P) {
+  constexpr int kThreads = 64 * NW;
   constexpr int KS = D / 16;            // k-steps of Q.K^T
   constexpr int DB = D / 32;            // 32-wide dim blocks of the output
   constexpr int KRow = D * 2 + 16;      // bytes per K row in LDS (padded)
@@ -84,8 +84,14 @@ void prefill_mfma_kernel(PrefillParams P) {
   constexpr int LPR = D / 8;            // threads per key row (16 B each)
   constexpr int KPP = kThreads / LPR;   // key rows per load pass
   constexpr int NPK = kBK / KPP;        // load passes for a K tile
-  constexpr int NVQ = (kBK / 4) * (D / 8);  // (key quad, dim octet) pairs in a V tile
-  __shared__ __attribute__((aligned(16))) char lds[2 * Stage];
+  constexpr int KPT = NW >= 8 ? 2 : 4;          // keys per thread in the V loader
+  constexpr int NVG = kBK / KPT;                // key groups per V tile
+  constexpr int NVQ = NVG * (D / 8);            // (key group, dim octet) pairs in a V tile
+  // Q fragments 0..QR-1 stay in registers; the rest are parked in LDS (per
+  // wave, lane-contiguous) to leave registers for the two-deep tile prefetch.
+  constexpr int QR = D == 128 ? 0 : KS;
+  constexpr int QBytes = (KS - QR) * 64 * 16;   // per wave
+  __shared__ __attribute__((aligned(16))) char lds[2 * Stage + NW * QBytes + 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -147,12 +153,16 @@ void prefill_mfma_kernel(PrefillParams P) {
   const uint16_t* cvbase = P.cv + kvrow * P.m_cap * D;
 
   // ---- Q fragment: B operand, lane holds Q[row j][16ks + 8hh .. +7]
-  bf16x8 qf[KS];
+  bf16x8 qf[QR > 0 ? QR : 1];
+  char* const qlds = lds + 2 * Stage + wave * QBytes;
   {
     const uint16_t* qrow = P.q + (((long)b * P.Hq + h) * L + t) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hh);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hh);
+      if (ks < QR) qf[ks] = x;
+      else *reinterpret_cast<bf16x8*>(qlds + ((ks - QR) * 64 + lane) * 16) = x;
+    }
   }
 
   // ---- tile loaders (global -> registers -> LDS)
@@ -160,18 +170,20 @@ void prefill_mfma_kernel(PrefillParams P) {
   // spans only its valid keys, so rows past the end (beyond the last visible
   // core, or past the last row of the workgroup) read as zero in hardware.
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 kreg[NPK];
-  u32x4 vreg[4];
+  // two register sets: the loads of a tile pair stay in flight for two
+  // iterations before they are written to LDS
+  u32x4 kreg[2][NPK];
+  u32x4 vreg[2][KPT];
   const int k_oct = tid % LPR;
   const int k_row0 = tid / LPR;
-  const int v_oct = tid / 16;   // dim octet
-  const int v_quad = tid % 16;  // key quad
+  const int v_oct = tid / NVG;  // dim octet
+  const int v_grp = tid % NVG;  // key group (KPT consecutive keys)
   const bool v_act = NVQ >= kThreads || tid < NVQ;  // all threads when D = 128
-  int koff[NPK], voff[4];
+  int koff[NPK], voff[KPT];
 #pragma unroll
   for (int i = 0; i < NPK; ++i) koff[i] = ((k_row0 + i * KPP) * D + 8 * k_oct) * 2;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = ((4 * v_quad + i) * D + 8 * v_oct) * 2;
+  for (int i = 0; i < KPT; ++i) voff[i] = ((KPT * v_grp + i) * D + 8 * v_oct) * 2;
 
   auto tile_core = [&](int it) { return it < n_ct; };
   auto tile_base = [&](int it) { return it < n_ct ? it * kBK : r0 + (it - n_ct) * kBK; };
@@ -183,41 +195,46 @@ void prefill_mfma_kernel(PrefillParams P) {
     const uint16_t* src = (core ? (values ? cvbase : ckbase) : (values ? vbase : kbase)) + (long)base * D;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, nvalid * D * 2, 0x00020000);
   };
-  auto load_k = [&](int it) {
+  auto load_k = [&](int set, int it) {
     const __amdgpu_buffer_rsrc_t r = rsrc(it, false);
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff[i], 0, 0);
+    for (int i = 0; i < NPK; ++i) kreg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff[i], 0, 0);
   };
-  auto load_v = [&](int it) {
+  auto load_v = [&](int set, int it) {
     if (v_act) {
       const __amdgpu_buffer_rsrc_t r = rsrc(it, true);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i], 0, 0);
+      for (int i = 0; i < KPT; ++i) vreg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i], 0, 0);
     }
   };
   // LDS: [K buffer 0 | K buffer 1 | V^T buffer 0 | V^T buffer 1]
   auto kbuf = [&](int i) { return lds + i * KBytes; };
   auto vbuf = [&](int i) { return lds + 2 * KBytes + i * VBytes; };
-  auto store_k = [&](int buf) {
+  auto store_k = [&](int set, int buf) {
     char* kt = kbuf(buf);
 #pragma unroll
     for (int i = 0; i < NPK; ++i)
-      *reinterpret_cast<u32x4*>(kt + (k_row0 + i * KPP) * KRow + 16 * k_oct) = kreg[i];
+      *reinterpret_cast<u32x4*>(kt + (k_row0 + i * KPP) * KRow + 16 * k_oct) = kreg[set][i];
   };
-  auto store_v = [&](int buf) {
+  auto store_v = [&](int set, int buf) {
     if (v_act) {
-      // keys 4q..4q+3 land at permuted positions kpos0..kpos0+3 (bits 2,3 of the key swapped);
-      // dim 8*v_oct+i of the four keys becomes one 8-byte row segment of V^T.
+      // keys KPT*g .. +KPT-1 land at consecutive permuted positions from kpos0
+      // (bits 2 and 3 of a key swapped); dim 8*v_oct+i of those keys becomes
+      // one 2*KPT-byte segment of V^T row 8*v_oct+i.
       char* vt = vbuf(buf);
-      const int q = v_quad;
-      const int kpos0 = 16 * (q >> 2) + 8 * (q & 1) + 4 * ((q >> 1) & 1);
+      const int k0 = KPT * v_grp;
+      const int kpos0 = (k0 & ~15) | ((k0 & 4) << 1) | ((k0 & 8) >> 1) | (k0 & 3);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int dw = i >> 1;
         const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(vreg[1][dw], vreg[0][dw], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(vreg[3][dw], vreg[2][dw], sel);
-        *reinterpret_cast<uint2*>(vt + (8 * v_oct + i) * kVRow + 2 * kpos0) = make_uint2(lo, hi);
+        const uint32_t lo = __builtin_amdgcn_perm(vreg[set][1][dw], vreg[set][0][dw], sel);
+        if constexpr (KPT == 4) {
+          const uint32_t hi = __builtin_amdgcn_perm(vreg[set][3][dw], vreg[set][2][dw], sel);
+          *reinterpret_cast<uint2*>(vt + (8 * v_oct + i) * kVRow + 2 * kpos0) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<uint32_t*>(vt + (8 * v_oct + i) * kVRow + 2 * kpos0) = lo;
+        }
       }
     }
   };
@@ -239,8 +256,10 @@ void prefill_mfma_kernel(PrefillParams P) {
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   // prologue: K(0) staged; V buffer 1 (read as "tile -1") cleared
-  load_k(0);
-  store_k(0);
+  load_k(0, 0);
+  store_k(0, 0);
+  load_k(1, 1);  // K(1), V(0): stored at the end of iteration 0
+  load_v(1, 0);
   for (int i = tid; i < VBytes / 16; i += kThreads)
     *reinterpret_cast<u32x4*>(vbuf(1) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
@@ -262,9 +281,11 @@ void prefill_mfma_kernel(PrefillParams P) {
   // and the exponentials share one scheduling region.
   bool grow_pending = false;
   float alpha_pending = 1.0f;
-  for (int it = 0; it < n_tiles; ++it) {
-    load_k(it + 1);  // empty past the last tile
-    load_v(it);
+  // set `cur` receives K(it+2), V(it+1); set `cur^1` holds K(it+1), V(it),
+  // issued one iteration earlier, and is written to LDS at the end
+  auto iteration = [&](int it, int cur) {
+    load_k(cur, it + 2);  // empty past the last tile
+    load_v(cur, it + 1);
     if (grow_pending) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -275,13 +296,17 @@ void prefill_mfma_kernel(PrefillParams P) {
     const char* vt_prev = vbuf((it + 1) & 1);
     f32x16 sx[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sx[kb][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 qb = ks < QR ? qf[ks < QR ? ks : 0]
+                                : *reinterpret_cast<const bf16x8*>(qlds + ((ks - QR) * 64 + lane) * 16);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + (32 * kb + j) * KRow + (16 * ks + 8 * hh) * 2);
-        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sx[kb], 0, 0, 0);
+        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb, sx[kb], 0, 0, 0);
       }
     }
     if (!tile_full(it)) {
@@ -319,27 +344,27 @@ void prefill_mfma_kernel(PrefillParams P) {
     l *= alpha;
     const float mc = (m == -INFINITY ? 0.f : m) * c;
     // P.V of tile it-1 interleaved by hand with tile it's exponentials: after
-    // each MFMA (32 cycles on the matrix core) come the two probabilities it
-    // can hide (2 fma, 2 exp, 1 convert, 1 dot2).  sched_barrier freezes that
-    // order; the V^T fragments of the next chunk are read one chunk ahead.
+    // each MFMA (32 cycles on the matrix core) come the probabilities it can
+    // hide (2 fma, 2 exp, 1 convert, 1 dot2 per pair).  sched_barrier freezes
+    // that order; V^T fragments are read two MFMAs ahead through a ring of 3.
     static_assert(DB == 2 || DB == 4, "head dim 64 or 128");
     constexpr int PPM = 8 / DB;  // probabilities per MFMA slot
-    bf16x8 vfr[2][DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      vfr[0][db] = *reinterpret_cast<const bf16x8*>(vt_prev + (32 * db + j) * kVRow + (8 * hh) * 2);
+    constexpr int NPV = 4 * DB;  // P.V MFMAs per tile
+    auto vfrag = [&](int n) {
+      const int cc = n / DB, db = n % DB;
+      return *reinterpret_cast<const bf16x8*>(vt_prev + (32 * db + j) * kVRow + (16 * cc + 8 * hh) * 2);
+    };
+    bf16x8 ring[3];
+    ring[0] = vfrag(0);
+    ring[1] = vfrag(1);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      if (cc + 1 < 4) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          vfr[(cc + 1) & 1][db] = *reinterpret_cast<const bf16x8*>(
-              vt_prev + (32 * db + j) * kVRow + (16 * (cc + 1) + 8 * hh) * 2);
-      }
       bf16x8 pnew;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[cc & 1][db], pr[cc], o[db], 0, 0, 0);
+        const int n = cc * DB + db;
+        if (n + 2 < NPV) ring[(n + 2) % 3] = vfrag(n + 2);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % 3], pr[cc], o[db], 0, 0, 0);
 #pragma unroll
         for (int e = db * PPM; e < db * PPM + PPM; e += 2) {
           const int r = (cc & 1) * 8 + e;
@@ -359,10 +384,16 @@ void prefill_mfma_kernel(PrefillParams P) {
     }
     grow_pending = __builtin_amdgcn_ballot_w64(grow) != 0;
     alpha_pending = alpha;
-    store_k((it + 1) & 1);
-    store_v(it & 1);
+    store_k(cur ^ 1, (it + 1) & 1);
+    store_v(cur ^ 1, it & 1);
     __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < n_tiles; it += 2) {
+    iteration(it, 0);
+    iteration(it + 1, 1);
   }
+  if (it < n_tiles) iteration(it, 0);
   if (grow_pending) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -401,6 +432,8 @@ void prefill_mfma_kernel(PrefillParams P) {
   }
 }
 
+constexpr int kWaves = 8;  // waves per workgroup
+
 int gcd_int(int a, int b) {
   while (b) {
     const int t = a % b;
@@ -430,8 +463,8 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
   P.w = sh.w;
   P.m_cap = m_cap;
   P.G = sh.G();
-  P.Hw = gcd_int(P.G, 4);
-  P.RP = 32 * (4 / P.Hw);
+  P.Hw = gcd_int(P.G, kWaves);
+  P.RP = 32 * (kWaves / P.Hw);
   P.nPB = (sh.L + P.RP - 1) / P.RP;
   P.nHG = P.G / P.Hw;
   P.U = sh.B * sh.Hkv * P.nHG;
@@ -440,11 +473,11 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
   const long blocks = (long)P.nPB * P.U;
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   if (sh.d == 64) {
-    if (out_dt == 1) hipLaunchKernelGGL((prefill_mfma_kernel<64, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, s, P);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<64, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, s, P);
+    if (out_dt == 1) hipLaunchKernelGGL((prefill_mfma_kernel<64, 1, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
+    else hipLaunchKernelGGL((prefill_mfma_kernel<64, 0, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
   } else {
-    if (out_dt == 1) hipLaunchKernelGGL((prefill_mfma_kernel<128, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, s, P);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<128, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, s, P);
+    if (out_dt == 1) hipLaunchKernelGGL((prefill_mfma_kernel<128, 1, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
+    else hipLaunchKernelGGL((prefill_mfma_kernel<128, 0, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
   }
   return hipGetLastError();
 }
