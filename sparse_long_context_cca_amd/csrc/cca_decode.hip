@@ -363,6 +363,250 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
 }
 
+// Pass 1 on the matrix cores (bf16, G <= 8 query heads per kv head).
+// grid = (splits, 1, B * Hkv); four waves per block.  Each wave streams its own
+// 32-key tiles of the block's key range -- no block barrier in the main loop:
+//   S^T (32 keys x 32 columns) = K . Q^T with v_mfma_f32_32x32x16_bf16; the
+//   columns are the kv head's G query heads, the rest zero (the matrix cores
+//   have ample headroom here: the loop is bound by HBM);
+//   K rows go straight from memory into the A operand registers;
+//   V rows are transposed through a wave-private LDS tile into V^T, with the
+//   key order permuted to match the score layout, so P^T is used in place as
+//   the B operand of O^T += V^T . P^T.
+// The four waves' online-softmax states are merged through LDS at the end.
+constexpr int kDecBK = 32;     // keys per wave tile
+constexpr int kDecVRow = 80;   // bytes per V^T row in LDS: 32 keys + 16 pad
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
+    const uint16_t* __restrict__ q_t, const uint16_t* __restrict__ k_t,
+    const uint16_t* __restrict__ v_t, uint16_t* __restrict__ ring_k, uint16_t* __restrict__ ring_v,
+    int R, uint16_t* __restrict__ ck, uint16_t* __restrict__ cv, int m_cap,
+    const int32_t* __restrict__ pos, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    float* __restrict__ ws_o, int Hq, int Hkv, int g, int w, int splits, float c) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  constexpr int KS = D / 16;            // k-steps of K.Q^T
+  constexpr int DB = D / 32;            // 32-dim blocks of O^T
+  constexpr int VBytes = D * kDecVRow;  // one wave's V^T tile
+  constexpr int NVP = (kDecBK / 4) * (D / 8) / 64;  // (key quad, dim octet) pairs per lane
+  // the V^T tiles, reused after the loop for the merge of the waves' states
+  constexpr int kMaxG = 8;
+  static_assert(4 * kMaxG * D * 4 <= 4 * VBytes, "merge area fits in the V^T tiles");
+  __shared__ __attribute__((aligned(16))) char lds[4 * VBytes];
+  __shared__ float red_m[4][kMaxG], red_l[4][kMaxG];
+
+  const int split = blockIdx.x;
+  const int bk = blockIdx.z;               // b * Hkv + kv head
+  const int b = bk / Hkv, hk = bk % Hkv;
+  const int G = Hq / Hkv;
+  const int h0 = hk * G;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 31, hh = lane >> 5;
+  const int t = pos[b];
+  const long st_base = ((long)b * Hq + h0) * splits + split;  // state of head h0
+
+  if (!decode_valid(t, g, m_cap)) {
+    if (threadIdx.x < G) ws_m[st_base + (long)threadIdx.x * splits] = NAN;
+    return;
+  }
+  const long bkl = bk;
+  const uint16_t* k_new = k_t + bkl * D;
+  const uint16_t* v_new = v_t + bkl * D;
+  uint16_t* rk = ring_k + bkl * R * D;
+  uint16_t* rv = ring_v + bkl * R * D;
+  uint16_t* ckb = ck + bkl * m_cap * D;
+  uint16_t* cvb = cv + bkl * m_cap * D;
+
+  // cache maintenance by the split-0 block of each (b, kv head)
+  if (split == 0) {
+    if (wave == 0) {
+      const long slot = (long)(t % R) * D;
+      for (int i = lane * 8; i < D; i += 64 * 8) {
+        *reinterpret_cast<uint4*>(rk + slot + i) = *reinterpret_cast<const uint4*>(k_new + i);
+        *reinterpret_cast<uint4*>(rv + slot + i) = *reinterpret_cast<const uint4*>(v_new + i);
+      }
+    } else if (wave == 1 && (t + 1) % g == 0) {
+      const int jn = (t + 1) / g - 1;
+      pool_new_group<1, D>(reinterpret_cast<const char*>(q_t + ((long)b * Hq + h0) * D),
+                           reinterpret_cast<const char*>(k_new), reinterpret_cast<const char*>(v_new),
+                           reinterpret_cast<const char*>(rk), reinterpret_cast<const char*>(rv),
+                           reinterpret_cast<char*>(ckb + (long)jn * D), reinterpret_cast<char*>(cvb + (long)jn * D),
+                           t, R, g, G, c);
+    }
+  }
+
+  const int nc = n_core(t, g, w);
+  const int lo = win_lo(t, w);
+  const int nvis = nc + (t - lo + 1);
+  const int chunk = (nvis + splits - 1) / splits;
+  const int f_begin = min(nvis, split * chunk);
+  const int f_end = min(nvis, f_begin + chunk);
+
+  // row pointer of visible key f (core, ring slot, or the new token)
+  auto krow = [&](int f, bool values) -> const uint16_t* {
+    if (f < nc) return (values ? cvb : ckb) + (long)f * D;
+    const int p = lo + (f - nc);
+    if (p == t) return values ? v_new : k_new;
+    return (values ? rv : rk) + (long)(p % R) * D;
+  };
+
+  // B operand: column j = query head h0 + j (zero past G); dims 16ks + 8hh ..
+  bf16x8 qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (j < G) {
+      qb[ks] = *reinterpret_cast<const bf16x8*>(q_t + ((long)b * Hq + h0 + j) * D + 16 * ks + 8 * hh);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qb[ks][e] = static_cast<__bf16>(0.0f);
+    }
+  }
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  char* vt = lds + wave * VBytes;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+  for (int f0 = f_begin + wave * kDecBK; f0 < f_end; f0 += 4 * kDecBK) {
+    // K rows -> A operand registers (zero past f_end)
+    u32x4 ka[KS];
+    {
+      const int f = f0 + j;
+      const bool ok = f < f_end;
+      const uint16_t* kr = ok ? krow(f, false) : k_new;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[ks] = ok ? *reinterpret_cast<const u32x4*>(kr + 16 * ks + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // V rows: lane covers NVP (key quad, dim octet) pairs
+    u32x4 va[NVP][4];
+#pragma unroll
+    for (int pi = 0; pi < NVP; ++pi) {
+      const int pair = lane + 64 * pi;
+      const int q = pair % (kDecBK / 4), oct = pair / (kDecBK / 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int f = f0 + 4 * q + i;
+        va[pi][i] = f < f_end ? *reinterpret_cast<const u32x4*>(krow(f, true) + 8 * oct)
+                              : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // S^T = K.Q^T
+    f32x16 sx;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sx[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks]), qb[ks], sx, 0, 0, 0);
+    // V^T into the wave's LDS tile (keys permuted: bits 2 and 3 swapped)
+#pragma unroll
+    for (int pi = 0; pi < NVP; ++pi) {
+      const int pair = lane + 64 * pi;
+      const int q = pair % (kDecBK / 4), oct = pair / (kDecBK / 4);
+      const int k0 = 4 * q;
+      const int kpos0 = (k0 & ~15) | ((k0 & 4) << 1) | ((k0 & 8) >> 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int dw = i >> 1;
+        const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t lo2 = __builtin_amdgcn_perm(va[pi][1][dw], va[pi][0][dw], sel);
+        const uint32_t hi2 = __builtin_amdgcn_perm(va[pi][3][dw], va[pi][2][dw], sel);
+        *reinterpret_cast<uint2*>(vt + (8 * oct + i) * kDecVRow + 2 * kpos0) = make_uint2(lo2, hi2);
+      }
+    }
+    // mask keys past the range; key of register r = 8(r/4) + 4hh + r%4
+    if (f0 + kDecBK > f_end) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kk = 8 * (r >> 2) + 4 * hh + (r & 3);
+        sx[r] = f0 + kk < f_end ? sx[r] : -INFINITY;
+      }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sx[r]);
+    {
+      auto rr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(rr[0]), __uint_as_float(rr[1]));
+    }
+    const float mnew = fmaxf(m, mt);
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+    m = mnew;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    const float mc = (m == -INFINITY ? 0.f : m) * c;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      bf16x2 pk;
+      pk[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sx[r], c, -mc)));
+      pk[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sx[r + 1], c, -mc)));
+      l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l, false);
+      pb[r >> 3][r & 7] = pk[0];
+      pb[r >> 3][(r & 7) + 1] = pk[1];
+    }
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + j) * kDecVRow + (16 * cc + 8 * hh) * 2);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], o[db], 0, 0, 0);
+      }
+  }
+
+  // merge the four waves: lane (column j, half hh) holds dims 32db + 8(r/4) + 4hh + r%4
+  {
+    auto rr = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+    l = __uint_as_float(rr[0]) + __uint_as_float(rr[1]);
+  }
+  __syncthreads();  // every wave is done with its V^T tile
+  float* red_o = reinterpret_cast<float*>(lds);   // [4 waves][kMaxG][D]
+  if (j < G) {
+    if (hh == 0) {
+      red_m[wave][j] = m;
+      red_l[wave][j] = l;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        red_o[(wave * kMaxG + j) * D + 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3)] = o[db][r];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int hcol = idx / D, e = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, red_m[wv][hcol]);
+    float lsum = 0.f, osum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        const float f = red_m[wv][hcol] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((red_m[wv][hcol] - M) * c);
+        lsum += red_l[wv][hcol] * f;
+        osum += red_o[(wv * kMaxG + hcol) * D + e] * f;
+      }
+    }
+    const long st = st_base + (long)hcol * splits;
+    ws_o[st * D + e] = osum;
+    if (e == 0) {
+      ws_m[st] = M * c;   // the combine pass works in log2 units
+      ws_l[st] = lsum;
+    }
+  }
+}
+
 // Pass 2.  One block of D threads per (b, query head).  The split states are
 // staged in LDS first so that the weighted sum issues independent loads.
 constexpr int kMaxSplits = 128;
@@ -450,11 +694,15 @@ void launch_split_g(int GT, const void* q_t, const void* k_t, const void* v_t, v
 }  // namespace
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int m_cap, int g, int w) {
-  (void)Hkv;
   (void)g;
-  // Upper bound of visible keys: every core slot plus the window.
+  // Enough blocks to fill the GPU (about 512 for 256 CUs), but no split
+  // shorter than 128 keys of the largest visible range (every core slot plus
+  // the window).
   const long nvis_max = (long)m_cap + w;
-  long splits = (nvis_max + 127) / 128;
+  const long bk = (long)B * Hkv;
+  long splits = (512 + bk - 1) / bk;
+  const long by_len = (nvis_max + 127) / 128;
+  if (splits > by_len) splits = by_len;
   if (splits < 1) splits = 1;
   if (splits > kMaxSplits) splits = kMaxSplits;
   DecodePlan p;
@@ -472,7 +720,21 @@ hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void
   float* ws_l = ws_m + (size_t)sh.B * sh.Hq * S;
   float* ws_o = ws_l + (size_t)sh.B * sh.Hq * S;
   const int GT = pick_gt(sh.G());
-  if (dt == 0) {
+  if (dt == 1 && sh.G() <= 8) {
+    const float c = kLog2e / sqrtf((float)sh.d);
+    dim3 grid(S, 1, sh.B * sh.Hkv);
+    const uint16_t* q16 = static_cast<const uint16_t*>(q_t);
+    const uint16_t* k16 = static_cast<const uint16_t*>(k_t);
+    const uint16_t* v16 = static_cast<const uint16_t*>(v_t);
+    uint16_t* rk16 = static_cast<uint16_t*>(ring_k);
+    uint16_t* rv16 = static_cast<uint16_t*>(ring_v);
+    uint16_t* ck16 = static_cast<uint16_t*>(ck);
+    uint16_t* cv16 = static_cast<uint16_t*>(cv);
+    if (sh.d == 64)
+      hipLaunchKernelGGL((decode_mfma_kernel<64>), grid, dim3(256), 0, s, q16, k16, v16, rk16, rv16, R, ck16, cv16, m_cap, pos, ws_m, ws_l, ws_o, sh.Hq, sh.Hkv, sh.g, sh.w, S, c);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<128>), grid, dim3(256), 0, s, q16, k16, v16, rk16, rv16, R, ck16, cv16, m_cap, pos, ws_m, ws_l, ws_o, sh.Hq, sh.Hkv, sh.g, sh.w, S, c);
+  } else if (dt == 0) {
     if (sh.d == 64) launch_split_g<0, 64>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
     else launch_split_g<0, 128>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
   } else {
