@@ -165,14 +165,39 @@ def bench_decode(cca, cfg, steps_timed=True):
     ms = e0.elapsed_time(e1)
     assert pos.tolist() == [L + S] * B
     assert torch.isfinite(out.float()).all()
+    out_eager = out.clone()
     total_bytes = sum(decode_step_bytes(cfg, L + i) for i in range(S))
     gbs = total_bytes / (ms * 1e-3) / 1e9
+
+    # the same 256 steps captured once in a HIP graph and replayed (no host
+    # launch work between steps; pos advances on the device)
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_all()
+    reset()
+    torch.cuda.synchronize()
+    graph.replay()                      # warm replay
+    reset()
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_g = e0.elapsed_time(e1)
+    assert pos.tolist() == [L + S] * B
+    assert torch.equal(out, out_eager), "graph replay differs from eager decode"
+    gbs_g = total_bytes / (ms_g * 1e-3) / 1e9
     return {
         "workload": cfg.name,
         "steps": S,
         "us_per_step": ms * 1e3 / S,
         "GB_per_s": gbs,
         "hbm_frac": gbs / PEAK_HBM_GBS,
+        "us_per_step_graph": ms_g * 1e3 / S,
+        "GB_per_s_graph": gbs_g,
+        "hbm_frac_graph": gbs_g / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": total_bytes / S,
         "launches_per_step": 2,
     }

@@ -332,6 +332,64 @@ def test_decode_out_of_capacity_gives_nan_and_no_writes():
     assert pos.tolist() == [11, 16]
 
 
+def test_decode_graph_replay_matches_eager():
+    """Decode steps captured in a HIP graph: every replay (with eager work and
+    synchronisation in between) reproduces the eager outputs bit for bit."""
+    say("decode graph replay")
+    B, Hq, Hkv, d, g, w, R, m_cap, steps = 2, 8, 2, 128, 4, 8, 8, 32, 12
+    pos0 = [20, 33]
+    T = max(pos0) + steps
+    cfg = cfg_of("graph", B, Hq, Hkv, T, d, g, w, "bf16", seed=41)
+    q, k, v = (x.to(DEV) for x in cca_inputs.prefill_inputs(cfg))
+    ck0 = torch.zeros((B, Hkv, m_cap, d), dtype=torch.bfloat16, device=DEV)
+    cv0 = torch.zeros_like(ck0)
+    Lh = max(pos0)
+    ckh, cvh, _ = gpu_pool(q[:, :, :Lh].contiguous(), k[:, :, :Lh].contiguous(), v[:, :, :Lh].contiguous(), g)
+    ck0[:, :, : Lh // g] = ckh[:, :, : Lh // g]
+    cv0[:, :, : Lh // g] = cvh[:, :, : Lh // g]
+    rk0 = torch.zeros((B, Hkv, R, d), dtype=torch.bfloat16, device=DEV)
+    rv0 = torch.zeros_like(rk0)
+    for b in range(B):
+        for p in range(pos0[b] - R, pos0[b]):
+            rk0[b, :, p % R] = k[b, :, p]
+            rv0[b, :, p % R] = v[b, :, p]
+    bidx = torch.arange(B, device=DEV)
+    qs = [q[bidx, :, torch.tensor([p + i for p in pos0], device=DEV)].contiguous() for i in range(steps)]
+    ks = [k[bidx, :, torch.tensor([p + i for p in pos0], device=DEV)].contiguous() for i in range(steps)]
+    vs = [v[bidx, :, torch.tensor([p + i for p in pos0], device=DEV)].contiguous() for i in range(steps)]
+    ck, cv, rk, rv = ck0.clone(), cv0.clone(), rk0.clone(), rv0.clone()
+    pos = torch.tensor(pos0, dtype=torch.int32, device=DEV)
+    ws = torch.empty(cca.cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w), dtype=torch.uint8, device=DEV)
+    outs = torch.empty((steps, B, Hq, d), dtype=torch.bfloat16, device=DEV)
+
+    def reset():
+        ck.copy_(ck0); cv.copy_(cv0); rk.copy_(rk0); rv.copy_(rv0)
+        pos.copy_(torch.tensor(pos0, dtype=torch.int32, device=DEV))
+        outs.zero_()
+
+    def run():
+        for i in range(steps):
+            cca.cca_attn_decode(qs[i], ks[i], vs[i], rk, rv, ck, cv, pos, outs[i], ws, g, w, advance_pos=True)
+
+    reset()
+    run()
+    torch.cuda.synchronize()
+    eager = outs.clone()
+    assert torch.isfinite(eager.float()).all()
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs, eager), f"replay {rep} differs"
+        assert pos.tolist() == [p + steps for p in pos0]
+
+
 def test_decode_c5_config():
     """The decode workload: batch 8, 32/8 heads, 65536 cached tokens (cores from
     the pool kernel, raw ring of 1024), 256 steps; every step, every (b, h)."""
