@@ -13,6 +13,7 @@ Prints ONE JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -30,6 +31,45 @@ import cca_inputs  # noqa: E402
 METRIC = "CCA prefill tokens/s + MFMA util at 128K (8B GQA shape, 1 GPU); decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from a committed counter summary under profiles/.
+
+    The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by
+    what the same counters read for a device copy of known size, plus a
+    digest of the kernel's sources; if their code has changed since the
+    counters were taken the figure no longer describes the kernel and None is
+    returned.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        key, val = line.split(":", 1)
+        fields[key.strip()] = val.strip()
+    try:
+        digest = code_digest(fields.get("sources", "").split())
+    except OSError:
+        return None
+    if digest != fields.get("kernel_sha256"):
+        return None
+    return int(fields["traffic_bytes"])
+
+
+def code_digest(sources):
+    """SHA-256 over the code lines of the given sources (// comments and blank
+    lines dropped, so that editing a comment keeps a counter figure valid)."""
+    h = hashlib.sha256()
+    for src in sources:
+        for line in open(os.path.join(ROOT, src), encoding="utf-8"):
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()
 
 
 def visible_pairs(L, g, w):
@@ -199,6 +239,7 @@ def bench_decode(cca, cfg, steps_timed=True):
         "GB_per_s_graph": gbs_g,
         "hbm_frac_graph": gbs_g / PEAK_HBM_GBS,
         "algorithmic_bytes_per_step": total_bytes / S,
+        "traffic_per_step": measured_traffic("decode_mfma_b8_ctx65536"),
         "launches_per_step": 2,
     }
 
@@ -289,16 +330,18 @@ def main():
                    "seq_len": cfg.L, "head_dim": cfg.d, "group": cfg.g, "window": cfg.w},
         "roofline": {
             "bound": "mfma",
-            "kernel": "prefill_mfma_kernel<128,1>",
+            "kernel": "prefill_mfma_kernel<128,1,8>",
             "achieved": tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic("prefill_mfma_gqa_L131072"),
+            "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flops_per_launch": flops,
             "avg_launch_ms": prefill_avg,
         },
         "pool": {"ms": pool_ms, "algorithmic_bytes": pool_bytes(cfg),
+                 "traffic": measured_traffic("pool_gqa_L131072"),
                  "GB_per_s": pool_bytes(cfg) / (pool_ms * 1e-3) / 1e9 if pool_ms > 0 else None},
     }
     if not args.no_decode:

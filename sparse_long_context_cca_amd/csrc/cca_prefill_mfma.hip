@@ -6,11 +6,11 @@
 // fused in a single softmax).
 //
 // Work decomposition
-//   * A workgroup (4 waves) owns 128 query rows that share one kv head: Hw
-//     query heads x (128/Hw) consecutive positions, Hw = gcd(G, 4).  Each wave
-//     owns 32 rows (one head, 32 consecutive positions).  With GQA the four
-//     waves are four query heads at the same positions, so every K/V tile
-//     staged in LDS serves all of them.
+//   * A workgroup (8 waves) owns 256 query rows that share one kv head: Hw
+//     query heads x (256/Hw) consecutive positions, Hw = gcd(G, 8).  Each wave
+//     owns 32 rows (one head, 32 consecutive positions).  With GQA several
+//     waves are query heads at the same positions, and every K/V tile staged
+//     in LDS serves all eight waves.
 //   * The workgroup walks the union of its rows' visible keys: first the core
 //     tiles 0..n_core(last row) (64 cores each), then the raw tiles covering
 //     win_lo(first row)..last row (64 positions each, 64-aligned).  Tiles that
@@ -22,13 +22,16 @@
 //     that XCD's L2.
 // Per 64-key tile and wave
 //   S^T (64 keys x 32 rows) = K_tile . Q^T with v_mfma_f32_32x32x16_bf16
-//   (A = K rows from LDS, B = the wave's Q fragment kept in registers);
+//   (A = K rows from LDS, B = the wave's Q fragment, parked in LDS at d=128);
 //   each lane then holds 32 scores of one query row, so the row max needs one
-//   exchange with lane l^32 and the row sum is kept per lane until the end.
+//   exchange with lane l^32, and the row sum is kept per lane until the end.
 //   P (bf16) is used in place as the B operand of O^T += V^T . P^T; V is
 //   stored transposed in LDS, its keys permuted to match the score layout.
-// Online softmax in the log2 domain with fp32 state; K/V tiles are double
-// buffered (global loads of tile i+1 are in flight while tile i computes).
+//   The P.V product of tile i-1 is interleaved with the exponentials of tile
+//   i, so the matrix cores work while the vector ALUs compute the softmax.
+// Online softmax in the log2 domain with fp32 state and a lazy rescale.  K
+// and V tiles are prefetched two deep through registers (buffer loads whose
+// range check zero-fills keys past the end) into double-buffered LDS.
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
 
