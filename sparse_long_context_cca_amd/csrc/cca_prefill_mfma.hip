@@ -194,9 +194,11 @@ void prefill_mfma_kernel(PrefillParams P) {
     const bool core = tile_core(it);
     const int base = tile_base(it);
     const int lim = core ? nc_hi : P_hi + 1;  // keys < lim are valid
-    const int nvalid = max(0, min(kBK, lim - base));  // 0 past the last tile
+    // The range is uniform; readfirstlane keeps it (and so the whole
+    // resource) in scalar registers, else every load becomes a waterfall loop.
+    const int nbytes = uni(max(0, min(kBK, lim - base)) * D * 2);  // 0 past the last tile
     const uint16_t* src = (core ? (values ? cvbase : ckbase) : (values ? vbase : kbase)) + (long)base * D;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, nvalid * D * 2, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, nbytes, 0x00020000);
   };
   auto load_k = [&](int set, int it) {
     const __amdgpu_buffer_rsrc_t r = rsrc(it, false);
