@@ -72,6 +72,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One wave load from a buffer straight into LDS: lane i's 16 bytes (from
+// byte voffset of the buffer, zeros when out of range) land at dst + 16 i.
+// dst must be the same for every lane.  (A plain function: the address-space
+// cast has no host form, and inside the kernel template it would drop the
+// host-side launch stub.)
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* dst, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voffset, 0, 0, 0);
+}
+
 // Two waves per SIMD (the accumulators stay in arch VGPRs, 256 per wave) so
 // that one wave's softmax overlaps the other's matrix ops.
 template <int D, int OT, int NW>
@@ -80,21 +89,20 @@ void prefill_mfma_kernel(PrefillParams P) {
   constexpr int kThreads = 64 * NW;
   constexpr int KS = D / 16;            // k-steps of Q.K^T
   constexpr int DB = D / 32;            // 32-wide dim blocks of the output
-  constexpr int KRow = D * 2 + 16;      // bytes per K row in LDS (padded)
+  constexpr int CPR = D / 8;            // 16-byte chunks per K row
+  constexpr int KRow = D * 2 + 16;      // bytes per K row in LDS (one chunk of padding)
   constexpr int KBytes = kBK * KRow;
+  constexpr int NKI = KBytes / 1024;    // 1 KB wave loads per K tile
+  static_assert(KBytes % 1024 == 0, "K tile is a whole number of wave loads");
+  constexpr int NKW = (NKI + NW - 1) / NW;  // K wave loads per wave (at most)
+  constexpr int NKMIN = NKI / NW;           // ... issued by every wave
   constexpr int VBytes = D * kVRow;
-  constexpr int Stage = KBytes + VBytes;
-  constexpr int LPR = D / 8;            // threads per key row (16 B each)
-  constexpr int KPP = kThreads / LPR;   // key rows per load pass
-  constexpr int NPK = kBK / KPP;        // load passes for a K tile
   constexpr int KPT = NW >= 8 ? 2 : 4;          // keys per thread in the V loader
   constexpr int NVG = kBK / KPT;                // key groups per V tile
   constexpr int NVQ = NVG * (D / 8);            // (key group, dim octet) pairs in a V tile
-  // Q fragments 0..QR-1 stay in registers; the rest are parked in LDS (per
-  // wave, lane-contiguous) to leave registers for the two-deep tile prefetch.
-  constexpr int QR = D == 128 ? 0 : KS;
-  constexpr int QBytes = (KS - QR) * 64 * 16;   // per wave
-  __shared__ __attribute__((aligned(16))) char lds[2 * Stage + NW * QBytes + 16];
+  // LDS: three K tiles (a ring: the tile in use and two in flight) and two
+  // transposed V tiles.
+  __shared__ __attribute__((aligned(16))) char lds[3 * KBytes + 2 * VBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -156,35 +164,33 @@ void prefill_mfma_kernel(PrefillParams P) {
   const uint16_t* cvbase = P.cv + kvrow * P.m_cap * D;
 
   // ---- Q fragment: B operand, lane holds Q[row j][16ks + 8hh .. +7]
-  bf16x8 qf[QR > 0 ? QR : 1];
-  char* const qlds = lds + 2 * Stage + wave * QBytes;
+  bf16x8 qf[KS];
   {
     const uint16_t* qrow = P.q + (((long)b * P.Hq + h) * L + t) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hh);
-      if (ks < QR) qf[ks] = x;
-      else *reinterpret_cast<bf16x8*>(qlds + ((ks - QR) * 64 + lane) * 16) = x;
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hh);
   }
 
-  // ---- tile loaders (global -> registers -> LDS)
+  // ---- tile loaders
   // Buffer loads: the resource of each tile starts at the tile's first key and
   // spans only its valid keys, so rows past the end (beyond the last visible
   // core, or past the last row of the workgroup) read as zero in hardware.
+  // K tiles go straight from memory into LDS (a wave load writes lane i's 16
+  // bytes at base + 16 i); the lanes that land on a row's padding chunk are
+  // given an offset past the range and write zeros.  V tiles pass through
+  // registers, where they are transposed.
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  // two register sets: the loads of a tile pair stay in flight for two
-  // iterations before they are written to LDS
-  u32x4 kreg[2][NPK];
   u32x4 vreg[2][KPT];
-  const int k_oct = tid % LPR;
-  const int k_row0 = tid / LPR;
   const int v_oct = tid / NVG;  // dim octet
   const int v_grp = tid % NVG;  // key group (KPT consecutive keys)
   const bool v_act = NVQ >= kThreads || tid < NVQ;  // all threads when D = 128
-  int koff[NPK], voff[KPT];
+  int koff[NKW], voff[KPT];
 #pragma unroll
-  for (int i = 0; i < NPK; ++i) koff[i] = ((k_row0 + i * KPP) * D + 8 * k_oct) * 2;
+  for (int i = 0; i < NKW; ++i) {
+    const int slot = (wave + NW * i) * 64 + lane;  // 16-byte slot of the LDS tile
+    const int row = slot / (CPR + 1), chunk = slot % (CPR + 1);
+    koff[i] = chunk < CPR ? (row * D + 8 * chunk) * 2 : 0x40000000;
+  }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) voff[i] = ((KPT * v_grp + i) * D + 8 * v_oct) * 2;
 
@@ -200,10 +206,17 @@ void prefill_mfma_kernel(PrefillParams P) {
     const uint16_t* src = (core ? (values ? cvbase : ckbase) : (values ? vbase : kbase)) + (long)base * D;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, nbytes, 0x00020000);
   };
-  auto load_k = [&](int set, int it) {
+  // LDS: [K ring 0 | K ring 1 | K ring 2 | V^T buffer 0 | V^T buffer 1]
+  auto kbuf = [&](int i) { return lds + i * KBytes; };
+  auto vbuf = [&](int i) { return lds + 3 * KBytes + i * VBytes; };
+  auto load_k = [&](int buf, int it) {  // K(it) -> ring slot buf (wave-uniform)
     const __amdgpu_buffer_rsrc_t r = rsrc(it, false);
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) kreg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff[i], 0, 0);
+    for (int i = 0; i < NKW; ++i) {
+      const int w = wave + NW * i;
+      if (NKI % NW == 0 || w < NKI)
+        lds_load16(r, kbuf(buf) + w * 1024, koff[i]);
+    }
   };
   auto load_v = [&](int set, int it) {
     if (v_act) {
@@ -211,15 +224,6 @@ void prefill_mfma_kernel(PrefillParams P) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) vreg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i], 0, 0);
     }
-  };
-  // LDS: [K buffer 0 | K buffer 1 | V^T buffer 0 | V^T buffer 1]
-  auto kbuf = [&](int i) { return lds + i * KBytes; };
-  auto vbuf = [&](int i) { return lds + 2 * KBytes + i * VBytes; };
-  auto store_k = [&](int set, int buf) {
-    char* kt = kbuf(buf);
-#pragma unroll
-    for (int i = 0; i < NPK; ++i)
-      *reinterpret_cast<u32x4*>(kt + (k_row0 + i * KPP) * KRow + 16 * k_oct) = kreg[set][i];
   };
   auto store_v = [&](int set, int buf) {
     if (v_act) {
@@ -260,14 +264,24 @@ void prefill_mfma_kernel(PrefillParams P) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // prologue: K(0) staged; V buffer 1 (read as "tile -1") cleared
+  // End of a pipeline stage: this wave's loads of K(it+1) into LDS and its
+  // writes of V^T(it) are complete, then the workgroup meets.  Loads finish in
+  // issue order, so allowing the loads issued since (K(it+2): at least NKMIN
+  // wave loads; V(it+1): KPT, by waves that load V) to stay in flight leaves
+  // K(it+1) landed.
+  constexpr int kInFlight = NKMIN + (NVQ >= kThreads ? KPT : 0);
+  auto sync_stage = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
+  };
+
+  // prologue: K(0) and K(1) into ring slots 0 and 1, V(0) into registers; V^T
+  // buffer 1 (read as "tile -1") cleared
   load_k(0, 0);
-  store_k(0, 0);
-  load_k(1, 1);  // K(1), V(0): stored at the end of iteration 0
+  load_k(1, 1);
   load_v(1, 0);
   for (int i = tid; i < VBytes / 16; i += kThreads)
     *reinterpret_cast<u32x4*>(vbuf(1) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  sync_stage();
   // probabilities of the previous tile (zeros before the first), bf16 B operands
   bf16x8 pr[4];
 #pragma unroll
@@ -275,8 +289,8 @@ void prefill_mfma_kernel(PrefillParams P) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) pr[cc][e] = static_cast<__bf16>(0.0f);
 
-  // Iteration it: LDS holds K(it) and V(it-1); the loads of K(it+1) and V(it)
-  // are in flight and stored at its end.  S = Q.K^T(it) on the matrix cores;
+  // Iteration it: LDS holds K(it) and V(it-1); K(it+1) is landing in the
+  // ring, and V(it), in registers, is written to LDS at its end.  S = Q.K^T(it) on the matrix cores;
   // then tile it's softmax on the vector ALUs while the matrix cores run P.V
   // of tile it-1.  Chunk cc of pr is consumed by that P.V just before tile
   // it's chunk cc overwrites it.  The rescale a new max demands (alpha) is
@@ -286,10 +300,11 @@ void prefill_mfma_kernel(PrefillParams P) {
   // and the exponentials share one scheduling region.
   bool grow_pending = false;
   float alpha_pending = 1.0f;
-  // set `cur` receives K(it+2), V(it+1); set `cur^1` holds K(it+1), V(it),
-  // issued one iteration earlier, and is written to LDS at the end
+  // Register set `cur` receives V(it+1); set `cur^1` holds V(it), issued one
+  // iteration earlier.  K(it) sits in ring slot it % 3 (kslot).
+  int kslot = 0;
   auto iteration = [&](int it, int cur) {
-    load_k(cur, it + 2);  // empty past the last tile
+    load_k(kslot == 0 ? 2 : kslot - 1, it + 2);  // empty past the last tile
     load_v(cur, it + 1);
     if (grow_pending) {
 #pragma unroll
@@ -297,7 +312,7 @@ void prefill_mfma_kernel(PrefillParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
     }
-    const char* kt = kbuf(it & 1);
+    const char* kt = kbuf(kslot);
     const char* vt_prev = vbuf((it + 1) & 1);
     f32x16 sx[2];
 #pragma unroll
@@ -306,8 +321,7 @@ void prefill_mfma_kernel(PrefillParams P) {
       for (int r = 0; r < 16; ++r) sx[kb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qb = ks < QR ? qf[ks < QR ? ks : 0]
-                                : *reinterpret_cast<const bf16x8*>(qlds + ((ks - QR) * 64 + lane) * 16);
+      const bf16x8 qb = qf[ks];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + (32 * kb + j) * KRow + (16 * ks + 8 * hh) * 2);
@@ -389,9 +403,9 @@ void prefill_mfma_kernel(PrefillParams P) {
     }
     grow_pending = __builtin_amdgcn_ballot_w64(grow) != 0;
     alpha_pending = alpha;
-    store_k(cur ^ 1, (it + 1) & 1);
     store_v(cur ^ 1, it & 1);
-    __syncthreads();
+    kslot = kslot == 2 ? 0 : kslot + 1;
+    sync_stage();
   };
   int it = 0;
   for (; it + 1 < n_tiles; it += 2) {
