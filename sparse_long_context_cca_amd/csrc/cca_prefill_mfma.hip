@@ -42,7 +42,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;       // keys per tile
-constexpr int kVRow = 144;    // bytes per transposed-V row: 64 keys + 16 pad
 constexpr float kLazyLog2 = 8.0f;  // rescale threshold of the running max, log2 units
 
 struct PrefillParams {
@@ -72,13 +71,43 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One wave load from a buffer straight into LDS: lane i's 16 bytes (from
-// byte voffset of the buffer, zeros when out of range) land at dst + 16 i.
-// dst must be the same for every lane.  (A plain function: the address-space
-// cast has no host form, and inside the kernel template it would drop the
-// host-side launch stub.)
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* dst, int voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voffset, 0, 0, 0);
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// 32-bit LDS address of a pointer into a __shared__ array.  (Address-space
+// casts live in plain functions: inside the kernel template they have no host
+// form and would drop the host-side launch stub.)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane s points at 4 consecutive 16-bit elements X_s[0..3]; lane i receives
+// X_{4e + (i%16)/4}[i % 4] for e = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
+}
+
+// Buffer resource over `nbytes` bytes from `base` (raw, no stride); reads past
+// the range return zeros.  Every word is uniform (scalar registers).
+__device__ __forceinline__ u32x4 buffer_desc(const void* base, int nbytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu;
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// One wave load from a buffer straight into LDS: lane i's 16 bytes (from byte
+// voffset of the buffer) land at LDS address m0 + 16 i; m0 is uniform.  Issued
+// as inline assembly so that the compiler does not see an LDS write: it would
+// otherwise make every later LDS read wait for all such loads in flight.  The
+// caller therefore orders these loads itself (a vmcnt wait and a barrier
+// before the data are read, and before the kernel ends).
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t m0, int voffset) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0));
 }
 
 // Two waves per SIMD (the accumulators stay in arch VGPRs, 256 per wave) so
@@ -96,13 +125,12 @@ void prefill_mfma_kernel(PrefillParams P) {
   static_assert(KBytes % 1024 == 0, "K tile is a whole number of wave loads");
   constexpr int NKW = (NKI + NW - 1) / NW;  // K wave loads per wave (at most)
   constexpr int NKMIN = NKI / NW;           // ... issued by every wave
-  constexpr int VBytes = D * kVRow;
-  constexpr int KPT = NW >= 8 ? 2 : 4;          // keys per thread in the V loader
-  constexpr int NVG = kBK / KPT;                // key groups per V tile
-  constexpr int NVQ = NVG * (D / 8);            // (key group, dim octet) pairs in a V tile
-  // LDS: three K tiles (a ring: the tile in use and two in flight) and two
-  // transposed V tiles.
-  __shared__ __attribute__((aligned(16))) char lds[3 * KBytes + 2 * VBytes];
+  constexpr int VBytes = kBK * D * 2;   // V tile: row-major, 64-byte blocks swizzled
+  constexpr int NVI = VBytes / 1024;    // 1 KB wave loads per V tile
+  static_assert(NVI % NW == 0, "V wave loads split evenly over the waves");
+  constexpr int NVW = NVI / NW;
+  // LDS: a ring of three K tiles and a ring of three V tiles
+  __shared__ __attribute__((aligned(16))) char lds[3 * KBytes + 3 * VBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,22 +197,25 @@ void prefill_mfma_kernel(PrefillParams P) {
     const uint16_t* qrow = P.q + (((long)b * P.Hq + h) * L + t) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hh);
+    // Use the fragments here, so that the compiler waits for these loads now:
+    // a wait placed at their first use inside the loop would also wait for the
+    // tile loads in flight there.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
-  // ---- tile loaders
-  // Buffer loads: the resource of each tile starts at the tile's first key and
-  // spans only its valid keys, so rows past the end (beyond the last visible
-  // core, or past the last row of the workgroup) read as zero in hardware.
-  // K tiles go straight from memory into LDS (a wave load writes lane i's 16
-  // bytes at base + 16 i); the lanes that land on a row's padding chunk are
-  // given an offset past the range and write zeros.  V tiles pass through
-  // registers, where they are transposed.
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 vreg[2][KPT];
-  const int v_oct = tid / NVG;  // dim octet
-  const int v_grp = tid % NVG;  // key group (KPT consecutive keys)
-  const bool v_act = NVQ >= kThreads || tid < NVQ;  // all threads when D = 128
-  int koff[NKW], voff[KPT];
+  // ---- tile loaders: buffer loads straight into LDS
+  // The resource of each tile starts at the tile's first key and spans only
+  // its valid keys, so rows past the end (beyond the last visible core, or
+  // past the last row of the workgroup) read as zero.  A wave load writes lane
+  // i's 16 bytes at base + 16 i, so the LDS layout is chosen by which chunk of
+  // the tile each lane fetches:
+  //   K: rows of D*2 bytes plus one 16-byte chunk of padding (the lanes that
+  //      land on it get an offset past the range and write zeros);
+  //   V: unpadded rows whose 64-byte blocks (32 dims) are XOR-swizzled by
+  //      vswz(row), so that the transposing reads below hit distinct banks.
+  auto vswz = [](int row) { return D == 128 ? (row & 3) : ((row >> 1) & 1); };
+  int koff[NKW], voff[NVW];
 #pragma unroll
   for (int i = 0; i < NKW; ++i) {
     const int slot = (wave + NW * i) * 64 + lane;  // 16-byte slot of the LDS tile
@@ -192,7 +223,11 @@ void prefill_mfma_kernel(PrefillParams P) {
     koff[i] = chunk < CPR ? (row * D + 8 * chunk) * 2 : 0x40000000;
   }
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) voff[i] = ((KPT * v_grp + i) * D + 8 * v_oct) * 2;
+  for (int i = 0; i < NVW; ++i) {
+    const int slot = (wave + NW * i) * 64 + lane;
+    const int row = slot / CPR, pos = (slot % CPR) >> 2, sub = slot & 3;
+    voff[i] = row * D * 2 + ((pos ^ vswz(row)) * 4 + sub) * 16;
+  }
 
   auto tile_core = [&](int it) { return it < n_ct; };
   auto tile_base = [&](int it) { return it < n_ct ? it * kBK : r0 + (it - n_ct) * kBK; };
@@ -200,52 +235,40 @@ void prefill_mfma_kernel(PrefillParams P) {
     const bool core = tile_core(it);
     const int base = tile_base(it);
     const int lim = core ? nc_hi : P_hi + 1;  // keys < lim are valid
-    // The range is uniform; readfirstlane keeps it (and so the whole
-    // resource) in scalar registers, else every load becomes a waterfall loop.
-    const int nbytes = uni(max(0, min(kBK, lim - base)) * D * 2);  // 0 past the last tile
+    const int nbytes = max(0, min(kBK, lim - base)) * D * 2;  // 0 past the last tile
     const uint16_t* src = (core ? (values ? cvbase : ckbase) : (values ? vbase : kbase)) + (long)base * D;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, nbytes, 0x00020000);
+    return buffer_desc(src, nbytes);
   };
-  // LDS: [K ring 0 | K ring 1 | K ring 2 | V^T buffer 0 | V^T buffer 1]
+  // LDS: [K ring 0 | K ring 1 | K ring 2 | V ring 0 | V ring 1 | V ring 2]
   auto kbuf = [&](int i) { return lds + i * KBytes; };
   auto vbuf = [&](int i) { return lds + 3 * KBytes + i * VBytes; };
-  auto load_k = [&](int buf, int it) {  // K(it) -> ring slot buf (wave-uniform)
-    const __amdgpu_buffer_rsrc_t r = rsrc(it, false);
+  auto load_k = [&](int slot, int it) {  // K(it) -> K ring slot (wave-uniform)
+    const u32x4 r = rsrc(it, false);
+    const uint32_t base = lds_addr(kbuf(slot));
 #pragma unroll
-    for (int i = 0; i < NKW; ++i) {
-      const int w = wave + NW * i;
-      if (NKI % NW == 0 || w < NKI)
-        lds_load16(r, kbuf(buf) + w * 1024, koff[i]);
-    }
+    for (int i = 0; i < NKMIN; ++i) lds_dma16(r, base + (wave + NW * i) * 1024, koff[i]);
+    if (NKW > NKMIN && wave < NKI - NW * NKMIN) lds_dma16(r, base + (wave + NW * NKMIN) * 1024, koff[NKW - 1]);
   };
-  auto load_v = [&](int set, int it) {
-    if (v_act) {
-      const __amdgpu_buffer_rsrc_t r = rsrc(it, true);
+  auto load_v = [&](int slot, int it) {  // V(it) -> V ring slot
+    const u32x4 r = rsrc(it, true);
+    const uint32_t base = lds_addr(vbuf(slot));
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) vreg[set][i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i], 0, 0);
-    }
+    for (int i = 0; i < NVW; ++i) lds_dma16(r, base + (wave + NW * i) * 1024, voff[i]);
   };
-  auto store_v = [&](int set, int buf) {
-    if (v_act) {
-      // keys KPT*g .. +KPT-1 land at consecutive permuted positions from kpos0
-      // (bits 2 and 3 of a key swapped); dim 8*v_oct+i of those keys becomes
-      // one 2*KPT-byte segment of V^T row 8*v_oct+i.
-      char* vt = vbuf(buf);
-      const int k0 = KPT * v_grp;
-      const int kpos0 = (k0 & ~15) | ((k0 & 4) << 1) | ((k0 & 8) >> 1) | (k0 & 3);
+  // V^T fragment for P.V MFMA (k-step cc, dim block db): lane (i, hh) needs
+  // V[key][dim 32 db + i] for the 8 keys 16cc + 8(e/4) + 4hh + e%4 (the key
+  // order of the score layout), i.e. two runs of 4 consecutive keys.  Each
+  // run is one transposing read in which lane s of a 16-lane group points at
+  // row 16cc + 8x + 4hh + s/4, dims 32db + 16((lane/16)%2) + 4(s%4) .. +3.
+  const int vs = lane & 15;
+  int vaddr[DB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int dw = i >> 1;
-        const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo = __builtin_amdgcn_perm(vreg[set][1][dw], vreg[set][0][dw], sel);
-        if constexpr (KPT == 4) {
-          const uint32_t hi = __builtin_amdgcn_perm(vreg[set][3][dw], vreg[set][2][dw], sel);
-          *reinterpret_cast<uint2*>(vt + (8 * v_oct + i) * kVRow + 2 * kpos0) = make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<uint32_t*>(vt + (8 * v_oct + i) * kVRow + 2 * kpos0) = lo;
-        }
-      }
-    }
+  for (int db = 0; db < DB; ++db)
+    vaddr[db] = (4 * hh + (vs >> 2)) * D * 2 + ((db ^ vswz(vs >> 2)) * 32 + 16 * ((lane >> 4) & 1) + 4 * (vs & 3)) * 2;
+  auto vfrag_at = [&](const char* vt, int cc, int db) {
+    const bf16x4 x0 = lds_read_tr16(vt + vaddr[db] + (16 * cc) * D * 2);
+    const bf16x4 x1 = lds_read_tr16(vt + vaddr[db] + (16 * cc + 8) * D * 2);
+    return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   };
   // Does tile it need a mask for this wave's rows?  (wave-uniform)  A tile
   // none of the wave's rows can see is simply fully masked.
@@ -264,24 +287,23 @@ void prefill_mfma_kernel(PrefillParams P) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // End of a pipeline stage: this wave's loads of K(it+1) into LDS and its
-  // writes of V^T(it) are complete, then the workgroup meets.  Loads finish in
-  // issue order, so allowing the loads issued since (K(it+2): at least NKMIN
-  // wave loads; V(it+1): KPT, by waves that load V) to stay in flight leaves
-  // K(it+1) landed.
-  constexpr int kInFlight = NKMIN + (NVQ >= kThreads ? KPT : 0);
+  // End of a pipeline stage: this wave's loads of the previous stage (K(it+1),
+  // V(it)) have landed in LDS, then the workgroup meets.  Loads finish in
+  // issue order, so allowing this stage's loads (K(it+2): at least NKMIN wave
+  // loads; V(it+1): NVW) to stay in flight is enough.
+  constexpr int kInFlight = NKMIN + NVW;
   auto sync_stage = [&]() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
   };
 
-  // prologue: K(0) and K(1) into ring slots 0 and 1, V(0) into registers; V^T
-  // buffer 1 (read as "tile -1") cleared
+  // prologue: K(0), K(1) into K slots 0, 1 and V(0) into V slot 0; V slot 2
+  // (read as "tile -1", with zero probabilities) cleared so it holds no NaN
   load_k(0, 0);
   load_k(1, 1);
-  load_v(1, 0);
+  load_v(0, 0);
   for (int i = tid; i < VBytes / 16; i += kThreads)
-    *reinterpret_cast<u32x4*>(vbuf(1) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-  sync_stage();
+    *reinterpret_cast<u32x4*>(vbuf(2) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NKMIN + NVW) : "memory");
   // probabilities of the previous tile (zeros before the first), bf16 B operands
   bf16x8 pr[4];
 #pragma unroll
@@ -289,8 +311,9 @@ void prefill_mfma_kernel(PrefillParams P) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) pr[cc][e] = static_cast<__bf16>(0.0f);
 
-  // Iteration it: LDS holds K(it) and V(it-1); K(it+1) is landing in the
-  // ring, and V(it), in registers, is written to LDS at its end.  S = Q.K^T(it) on the matrix cores;
+  // Iteration it: LDS holds K(it) (K slot it%3) and V(it-1) (V slot
+  // (it+2)%3); K(it+1) and V(it) are landing.  It issues the loads of K(it+2)
+  // and V(it+1) into the slots freed by tiles it-1 and it-2.  S = Q.K^T(it) on the matrix cores;
   // then tile it's softmax on the vector ALUs while the matrix cores run P.V
   // of tile it-1.  Chunk cc of pr is consumed by that P.V just before tile
   // it's chunk cc overwrites it.  The rescale a new max demands (alpha) is
@@ -300,12 +323,11 @@ void prefill_mfma_kernel(PrefillParams P) {
   // and the exponentials share one scheduling region.
   bool grow_pending = false;
   float alpha_pending = 1.0f;
-  // Register set `cur` receives V(it+1); set `cur^1` holds V(it), issued one
-  // iteration earlier.  K(it) sits in ring slot it % 3 (kslot).
-  int kslot = 0;
-  auto iteration = [&](int it, int cur) {
-    load_k(kslot == 0 ? 2 : kslot - 1, it + 2);  // empty past the last tile
-    load_v(cur, it + 1);
+  int kslot = 0;  // it % 3
+  auto iteration = [&](int it) {
+    const int prev = kslot == 0 ? 2 : kslot - 1, next = kslot == 2 ? 0 : kslot + 1;
+    load_k(prev, it + 2);  // empty (zeros) past the last tile
+    load_v(next, it + 1);
     if (grow_pending) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -313,7 +335,7 @@ void prefill_mfma_kernel(PrefillParams P) {
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
     }
     const char* kt = kbuf(kslot);
-    const char* vt_prev = vbuf((it + 1) & 1);
+    const char* vt_prev = vbuf(prev);
     f32x16 sx[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -369,10 +391,7 @@ void prefill_mfma_kernel(PrefillParams P) {
     static_assert(DB == 2 || DB == 4, "head dim 64 or 128");
     constexpr int PPM = 8 / DB;  // probabilities per MFMA slot
     constexpr int NPV = 4 * DB;  // P.V MFMAs per tile
-    auto vfrag = [&](int n) {
-      const int cc = n / DB, db = n % DB;
-      return *reinterpret_cast<const bf16x8*>(vt_prev + (32 * db + j) * kVRow + (16 * cc + 8 * hh) * 2);
-    };
+    auto vfrag = [&](int n) { return vfrag_at(vt_prev, n / DB, n % DB); };
     bf16x8 ring[3];
     ring[0] = vfrag(0);
     ring[1] = vfrag(1);
@@ -403,30 +422,27 @@ void prefill_mfma_kernel(PrefillParams P) {
     }
     grow_pending = __builtin_amdgcn_ballot_w64(grow) != 0;
     alpha_pending = alpha;
-    store_v(cur ^ 1, it & 1);
-    kslot = kslot == 2 ? 0 : kslot + 1;
+    kslot = next;
     sync_stage();
   };
-  int it = 0;
-  for (; it + 1 < n_tiles; it += 2) {
-    iteration(it, 0);
-    iteration(it + 1, 1);
-  }
-  if (it < n_tiles) iteration(it, 0);
+  for (int it = 0; it < n_tiles; ++it) iteration(it);
+  // the loads issued for tiles past the end must land before the workgroup's
+  // LDS can be handed to another
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (grow_pending) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
   }
+  {
+    const char* vt = vbuf(kslot == 0 ? 2 : kslot - 1);  // V(n_tiles - 1)
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
+    for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const char* vt = vbuf((n_tiles - 1) & 1);
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + j) * kVRow + (16 * cc + 8 * hh) * 2);
-      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pr[cc], o[db], 0, 0, 0);
-    }
+      for (int db = 0; db < DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag_at(vt, cc, db), pr[cc], o[db], 0, 0, 0);
+  }
 
   // ---- normalise and store: lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
   const float ltot = pair_sum(l);
