@@ -44,8 +44,12 @@ def _softmax_list(s):
     return [x / tot for x in e]
 
 
-def pool(Q, K, V, g: int):
-    """Nested lists / arrays indexed [b][h][t][e]; returns CK, CV, A as lists."""
+def pool(Q, K, V, g: int, mode: str = "softmax"):
+    """Nested lists / arrays indexed [b][h][t][e]; returns CK, CV, A as lists.
+
+    mode "softmax": weights from the softmax of the mean last-token query;
+    "softmax_heads": mean over the heads of each head's own softmax;
+    "mean": equal weights; "max": element-wise maximum (A holds None)."""
     B, Hq, L, d = len(Q), len(Q[0]), len(Q[0][0]), len(Q[0][0][0])
     Hkv = len(K[0])
     G = Hq // Hkv
@@ -57,13 +61,32 @@ def pool(Q, K, V, g: int):
             j = 0
             while (j + 1) * g <= L:
                 last = (j + 1) * g - 1
-                qbar = [0.0] * d
-                for hq in range(hk * G, hk * G + G):
-                    for e in range(d):
-                        qbar[e] += float(Q[b][hq][last][e]) / G
                 members = list(range(j * g, j * g + g))
-                scores = [_dot(qbar, K[b][hk][i]) / math.sqrt(d) for i in members]
-                a = _softmax_list(scores)
+                heads = list(range(hk * G, hk * G + G))
+                if mode == "max":
+                    ck = [max(float(K[b][hk][i][e]) for i in members) for e in range(d)]
+                    cv = [max(float(V[b][hk][i][e]) for i in members) for e in range(d)]
+                    ck_h.append(ck)
+                    cv_h.append(cv)
+                    a_h.append(None)
+                    j += 1
+                    continue
+                if mode == "softmax":
+                    qbar = [0.0] * d
+                    for hq in heads:
+                        for e in range(d):
+                            qbar[e] += float(Q[b][hq][last][e]) / G
+                    a = _softmax_list([_dot(qbar, K[b][hk][i]) / math.sqrt(d) for i in members])
+                elif mode == "softmax_heads":
+                    a = [0.0] * g
+                    for hq in heads:
+                        ah = _softmax_list([_dot(Q[b][hq][last], K[b][hk][i]) / math.sqrt(d) for i in members])
+                        for n in range(g):
+                            a[n] += ah[n] / G
+                elif mode == "mean":
+                    a = [1.0 / g] * g
+                else:
+                    raise ValueError(mode)
                 ck = [sum(a[n] * float(K[b][hk][i][e]) for n, i in enumerate(members)) for e in range(d)]
                 cv = [sum(a[n] * float(V[b][hk][i][e]) for n, i in enumerate(members)) for e in range(d)]
                 ck_h.append(ck)

@@ -49,6 +49,17 @@ Readings of what the pages leave open (each is a choice, stated once here):
        heads that share the kv head.  PARITY UNPINNED by the pages: pinned
        only by the G = 1 reduction and by "G identical heads == one head".
   R-9  Query head h reads kv head floor(h / G).
+  R-13 Pooling variants.  The rebuttal (answer on Table 3) names max pooling
+       and mean pooling as ablation alternatives to global-aware pooling,
+       without formulas.  Plainest reading: over the g tokens of a group, the
+       element-wise maximum (mode "max") or the arithmetic mean (mode
+       "mean") of K and of V, each taken separately.  The rebuttal's GQA
+       answer leaves the rule open; besides R-8 (mode "softmax", the default)
+       the oracle offers the other plain rule, the mean over the G query heads
+       of each head's own pooling softmax (mode "softmax_heads").  These
+       modes are pinned by brute force, by their reductions to one another
+       and by invariants; the pages fix none of their values (PARITY
+       UNPINNED by the pages, like R-8).
   R-10 Decode row t is prefill row t of the sequence extended to t+1 tokens;
        the core of a group that completes at t is pooled with q_t and is not
        visible to t itself.
@@ -121,22 +132,29 @@ def _softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
 # ------------------------------------------------------------------- pooling
 
 
-def pool_core(Q, K, V, g: int):
-    """Global-aware pooling ([digest], Method, pooling formula).
+POOL_MODES = ("softmax", "softmax_heads", "mean", "max")
+
+
+def pool_core(Q, K, V, g: int, mode: str = "softmax"):
+    """Global-aware pooling ([digest], Method, pooling formula) and the
+    variants of R-13 (``mode``).
 
     Q [B,Hq,L,d]; K, V [B,Hkv,L,d] (any float dtype; widened to fp64).
-    Returns CK, CV [B,Hkv,m,d] and the pooling weights A [B,Hkv,m,g], m = L//g.
+    Returns CK, CV [B,Hkv,m,d] and the pooling weights A [B,Hkv,m,g], m = L//g
+    (NaN for mode "max", which has no weights).
     """
     B, Hq, L, d = Q.shape
     m = L // g
     last = np.array([group_last(j, g) for j in range(m)], dtype=np.int64)
     # query of each group's last token, one per query head: [B,Hq,m,d]
-    return pool_from_last(Q[:, :, last, :], K, V, g)
+    return pool_from_last(Q[:, :, last, :], K, V, g, mode)
 
 
-def pool_from_last(q_last, K, V, g: int):
+def pool_from_last(q_last, K, V, g: int, mode: str = "softmax"):
     """Pooling given the last-token query rows: q_last[:, h, j] is the query of
     head h at token (j+1)g-1.  Same outputs as ``pool_core``."""
+    if mode not in POOL_MODES:
+        raise ValueError(f"unknown pooling mode {mode!r}")
     B, Hq, m, d = q_last.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
@@ -152,8 +170,20 @@ def pool_from_last(q_last, K, V, g: int):
             q_bar = _f64(q_last[b, hk * G : hk * G + G]).mean(axis=0)         # [m, d]
             Kg = _f64(K[b, hk, : m * g, :]).reshape(m, g, d)                  # group i = rows ig..ig+g-1
             Vg = _f64(V[b, hk, : m * g, :]).reshape(m, g, d)
-            s = (Kg * q_bar[:, None, :]).sum(axis=-1) / math.sqrt(d)          # [m, g]
-            a = _softmax(s, axis=-1)
+            if mode == "max":                                                 # R-13
+                A[b, hk] = np.nan
+                CK[b, hk] = Kg.max(axis=1)
+                CV[b, hk] = Vg.max(axis=1)
+                continue
+            if mode == "softmax":
+                s = (Kg * q_bar[:, None, :]).sum(axis=-1) / math.sqrt(d)      # [m, g]
+                a = _softmax(s, axis=-1)
+            elif mode == "softmax_heads":                                     # R-13: mean of per-head softmaxes
+                qs = _f64(q_last[b, hk * G : hk * G + G])                     # [G, m, d]
+                s = (Kg[None] * qs[:, :, None, :]).sum(axis=-1) / math.sqrt(d)  # [G, m, g]
+                a = _softmax(s, axis=-1).mean(axis=0)
+            else:                                                             # "mean"
+                a = np.full((m, g), 1.0 / g)
             A[b, hk] = a
             CK[b, hk] = (a[:, :, None] * Kg).sum(axis=1)
             CV[b, hk] = (a[:, :, None] * Vg).sum(axis=1)

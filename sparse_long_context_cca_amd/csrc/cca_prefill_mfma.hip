@@ -22,16 +22,17 @@
 //     that XCD's L2.
 // Per 64-key tile and wave
 //   S^T (64 keys x 32 rows) = K_tile . Q^T with v_mfma_f32_32x32x16_bf16
-//   (A = K rows from LDS, B = the wave's Q fragment, parked in LDS at d=128);
+//   (A = K rows from LDS, B = the wave's Q fragments, held in registers);
 //   each lane then holds 32 scores of one query row, so the row max needs one
 //   exchange with lane l^32, and the row sum is kept per lane until the end.
-//   P (bf16) is used in place as the B operand of O^T += V^T . P^T; V is
-//   stored transposed in LDS, its keys permuted to match the score layout.
-//   The P.V product of tile i-1 is interleaved with the exponentials of tile
-//   i, so the matrix cores work while the vector ALUs compute the softmax.
+//   P (bf16) is used in place as the B operand of O^T += V^T . P^T; the V^T
+//   operand comes from a row-major V tile through transposing LDS reads that
+//   follow the key order of the score layout.  The P.V product of tile i-1
+//   is interleaved with the exponentials of tile i, so the matrix cores work
+//   while the vector ALUs compute the softmax.
 // Online softmax in the log2 domain with fp32 state and a lazy rescale.  K
-// and V tiles are prefetched two deep through registers (buffer loads whose
-// range check zero-fills keys past the end) into double-buffered LDS.
+// and V tiles are loaded straight from memory into three-slot LDS rings, two
+// tiles ahead (buffer loads whose range check zero-fills keys past the end).
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
 

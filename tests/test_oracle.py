@@ -332,9 +332,78 @@ def pin_decode_is_prefill_row(o):
     return fails
 
 
+def pin_pool_modes(o):
+    """Pooling variants (reading R-13): each mode against the scalar brute
+    force; their reductions to one another; and invariants that fix them."""
+    fails = []
+    B, Hq, Hkv, L, d, g = 2, 6, 2, 22, 5, 4
+    Q = _rand(81, (B, Hq, L, d), 2.0)
+    K, V = _rand(82, (B, Hkv, L, d)), _rand(83, (B, Hkv, L, d))
+    m = L // g
+    for mode in ("softmax", "softmax_heads", "mean", "max"):
+        ck, cv, a = o.pool_core(Q, K, V, g, mode)
+        bk, bv, ba = brute.pool(Q, K, V, g, mode)
+        for name, x, y in (("CK", ck, bk), ("CV", cv, bv)):
+            e = _close(x, np.array(y), 1e-12)
+            if e:
+                fails.append(f"{mode} {name} vs brute force: {e}")
+        if mode != "max":
+            e = _close(a, np.array(ba), 1e-12)
+            if e:
+                fails.append(f"{mode} weights vs brute force: {e}")
+            if np.any(a < 0) or _close(a.sum(-1), np.ones((B, Hkv, m)), 1e-12):
+                fails.append(f"{mode} weights are not a distribution")
+    # mean pooling is softmax pooling with a zero query (equal scores)
+    e = _close(o.pool_core(Q, K, V, g, "mean")[0], o.pool_core(np.zeros_like(Q), K, V, g, "softmax")[0], 1e-12)
+    if e:
+        fails.append(f"mean != softmax with zero query: {e}")
+    # one query head per kv head: the two softmax rules coincide
+    Q1 = Q[:, :Hkv]
+    e = _close(o.pool_core(Q1, K, V, g, "softmax_heads")[0], o.pool_core(Q1, K, V, g, "softmax")[0], 1e-12)
+    if e:
+        fails.append(f"softmax_heads != softmax at G=1: {e}")
+    # G identical heads: both rules equal the single-head pooling
+    Qrep = np.repeat(Q1, 3, axis=1)
+    for mode in ("softmax", "softmax_heads"):
+        e = _close(o.pool_core(Qrep, K, V, g, mode)[0], o.pool_core(Q1, K, V, g, "softmax")[0], 1e-12)
+        if e:
+            fails.append(f"{mode} with identical heads: {e}")
+    # different heads: the two rules differ (softmax is not linear in its logits)
+    if _close(o.pool_core(Q, K, V, g, "softmax_heads")[0], o.pool_core(Q, K, V, g, "softmax")[0], 1e-6) is None:
+        fails.append("softmax_heads equals softmax for distinct heads")
+    # max: every member is below the result, and each component is attained
+    ck, cv, _ = o.pool_core(Q, K, V, g, "max")
+    Kg = K[:, :, : m * g].reshape(B, Hkv, m, g, d)
+    Vg = V[:, :, : m * g].reshape(B, Hkv, m, g, d)
+    for name, x, grp in (("CK", ck, Kg), ("CV", cv, Vg)):
+        if np.any(grp > x[:, :, :, None, :]):
+            fails.append(f"max {name}: a member exceeds the pooled value")
+        if not np.all(np.any(grp == x[:, :, :, None, :], axis=3)):
+            fails.append(f"max {name}: a pooled component is not attained")
+    # a group of identical tokens pools to that token in every mode; a joint
+    # permutation of the tokens inside each group changes nothing
+    Kc = np.repeat(K[:, :, ::g][:, :, :m], g, axis=2)
+    Vc = np.repeat(V[:, :, ::g][:, :, :m], g, axis=2)
+    perm = np.concatenate([j * g + np.roll(np.arange(g), 1) for j in range(m)] + [np.arange(m * g, L)])
+    Qp = Q.copy()
+    Qp[:, :, perm] = Q  # keep each group's last-token query where the pooling looks for it
+    Qp[:, :, [j * g + g - 1 for j in range(m)]] = Q[:, :, [j * g + g - 1 for j in range(m)]]
+    for mode in ("softmax", "softmax_heads", "mean", "max"):
+        e = _close(o.pool_core(Q[:, :, : m * g], Kc, Vc, g, mode)[0], Kc[:, :, ::g], 1e-12)
+        if e:
+            fails.append(f"{mode}: identical tokens: {e}")
+        base = o.pool_core(Q, K, V, g, mode)
+        permd = o.pool_core(Q, K[:, :, perm], V[:, :, perm], g, mode)
+        for x, y in zip(base[:2], permd[:2]):
+            e = _close(x, y, 1e-12)
+            if e:
+                fails.append(f"{mode}: permutation inside groups: {e}")
+    return fails
+
+
 PINS = [pin_visibility_vs_sets, pin_pair_counts, pin_kv_cache_size, pin_pool_worked_example,
         pin_pool_invariants, pin_pool_gqa, pin_reduces_to_full_causal, pin_visible_set_one_hot,
-        pin_brute_force, pin_convex_hull, pin_decode_is_prefill_row]
+        pin_brute_force, pin_convex_hull, pin_decode_is_prefill_row, pin_pool_modes]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -360,19 +429,38 @@ MUTATIONS = {
 }
 
 
-def _pool_no_scale(Q, K, V, g):
+def _pool_no_scale(Q, K, V, g, mode="softmax"):
     B, Hq, L, d = Q.shape
-    return _ORIG_POOL(Q * math.sqrt(d), K, V, g)
+    return _ORIG_POOL(Q * math.sqrt(d), K, V, g, mode)
 
 
-def _pool_swapped_kv(Q, K, V, g):
-    ck, cv, a = _ORIG_POOL(Q, K, V, g)
+def _pool_swapped_kv(Q, K, V, g, mode="softmax"):
+    ck, cv, a = _ORIG_POOL(Q, K, V, g, mode)
     return cv, ck, a
 
 
-def _pool_first_head_only(Q, K, V, g):
+def _pool_first_head_only(Q, K, V, g, mode="softmax"):
     G = Q.shape[1] // K.shape[1]
-    return _ORIG_POOL(np.repeat(Q[:, ::G], G, axis=1), K, V, g)
+    return _ORIG_POOL(np.repeat(Q[:, ::G], G, axis=1), K, V, g, mode)
+
+
+def _pool_max_is_min(Q, K, V, g, mode="softmax"):
+    if mode != "max":
+        return _ORIG_POOL(Q, K, V, g, mode)
+    ck, cv, a = _ORIG_POOL(-Q, -K, -V, g, mode)
+    return -ck, -cv, a
+
+
+def _pool_heads_average_logits(Q, K, V, g, mode="softmax"):
+    # mean of the per-head scores instead of the mean of the per-head softmaxes
+    return _ORIG_POOL(Q, K, V, g, "softmax" if mode == "softmax_heads" else mode)
+
+
+def _pool_mean_over_g_minus_1(Q, K, V, g, mode="softmax"):
+    ck, cv, a = _ORIG_POOL(Q, K, V, g, mode)
+    if mode == "mean" and g > 1:
+        return ck * g / (g - 1), cv * g / (g - 1), a * g / (g - 1)
+    return ck, cv, a
 
 
 def _rows_transposed_heads(Q, K, V, CK, CV, g, w, ts):
@@ -392,6 +480,9 @@ FN_MUTATIONS = {
     "pooling scores not scaled by 1/sqrt(d)": ("pool_core", _pool_no_scale),
     "core K and V swapped": ("pool_core", _pool_swapped_kv),
     "GQA pooling query from first head only": ("pool_core", _pool_first_head_only),
+    "max pooling takes the minimum": ("pool_core", _pool_max_is_min),
+    "per-head softmax rule averages logits": ("pool_core", _pool_heads_average_logits),
+    "mean pooling divides by g-1": ("pool_core", _pool_mean_over_g_minus_1),
     "query head -> kv head map transposed": ("attn_rows", _rows_transposed_heads),
 }
 
