@@ -64,6 +64,28 @@ typedef enum cca_status {
 
 typedef enum cca_dtype { CCA_F32 = 0, CCA_BF16 = 1 } cca_dtype;
 
+/*
+ * Pooling rule for the core token of a group (used by cca_pool_core_ex and
+ * cca_attn_decode_ex; the other entry points use CCA_POOL_SOFTMAX):
+ *   CCA_POOL_SOFTMAX        global-aware pooling: a = softmax(qbar . K / sqrt(d))
+ *                           with qbar the mean over the G query heads of the
+ *                           group's last-token query (digest, "Method",
+ *                           pooling formula; one query per kv head).
+ *   CCA_POOL_SOFTMAX_HEADS  a = mean over the G heads of softmax(q_h . K /
+ *                           sqrt(d)); the rebuttal's GQA answer leaves this
+ *                           rule open.  Needs G <= 8.
+ *   CCA_POOL_MEAN           a = 1/g (the mean-pooling ablation the rebuttal
+ *   CCA_POOL_MAX            names, answer on Table 3); element-wise maximum
+ *                           over the group of K and of V (max-pooling
+ *                           ablation), which has no weights.
+ */
+typedef enum cca_pool_mode {
+  CCA_POOL_SOFTMAX = 0,
+  CCA_POOL_SOFTMAX_HEADS = 1,
+  CCA_POOL_MEAN = 2,
+  CCA_POOL_MAX = 3
+} cca_pool_mode;
+
 /* Library version (major*10000 + minor*100 + patch). */
 int cca_version(void);
 
@@ -97,6 +119,17 @@ cca_status cca_visibility_table(int L, int g, int w, int32_t* n_core, int32_t* w
 cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core_k, void* core_v,
                          int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d, int g,
                          cca_dtype dt, void* stream);
+
+/*
+ * cca_pool_core_ex - cca_pool_core with a pooling rule (cca_pool_mode above).
+ *   weights receives the a of the rule; it must be NULL for CCA_POOL_MAX.
+ *   q is not read by CCA_POOL_MEAN and CCA_POOL_MAX (it may be NULL there).
+ * Errors: as cca_pool_core; INVALID_ARG for an unknown mode or weights with
+ *   CCA_POOL_MAX; UNSUPPORTED for CCA_POOL_SOFTMAX_HEADS with G > 8.
+ */
+cca_status cca_pool_core_ex(const void* q, const void* k, const void* v, void* core_k,
+                            void* core_v, int m_cap, float* weights, int B, int Hq, int Hkv, int L,
+                            int d, int g, cca_dtype dt, int mode, void* stream);
 
 /*
  * cca_attn_prefill - causal prefill of the fused CCA attention (digest,
@@ -157,6 +190,19 @@ cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, vo
                            int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
                            void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
                            int g, int w, cca_dtype dt, void* stream);
+
+/*
+ * cca_attn_decode_ex - cca_attn_decode whose on-completion pooling (step 2)
+ * follows the rule `pool_mode` (cca_pool_mode above), so that a decode loop
+ * continues a cache built by cca_pool_core_ex with the same rule.
+ * Errors: as cca_attn_decode; INVALID_ARG for an unknown mode; UNSUPPORTED
+ *   for CCA_POOL_SOFTMAX_HEADS with G > 8.
+ */
+cca_status cca_attn_decode_ex(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                              void* ring_v, int R, void* core_k, void* core_v, int m_cap,
+                              int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                              void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                              int d, int g, int w, cca_dtype dt, int pool_mode, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,10 +17,11 @@ LIB_PATH = os.path.join(_PKG, "libcca.so")
 
 CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_CAPACITY, CCA_ERR_HIP = range(5)
 CCA_F32, CCA_BF16 = 0, 1
+CCA_POOL_SOFTMAX, CCA_POOL_SOFTMAX_HEADS, CCA_POOL_MEAN, CCA_POOL_MAX = range(4)
 
 EXPORTS = ["cca_version", "cca_status_string", "cca_last_error", "cca_visibility_table",
-           "cca_pool_core", "cca_attn_prefill", "cca_attn_prefill_ex", "cca_decode_workspace_bytes",
-           "cca_attn_decode"]
+           "cca_pool_core", "cca_pool_core_ex", "cca_attn_prefill", "cca_attn_prefill_ex",
+           "cca_decode_workspace_bytes", "cca_attn_decode", "cca_attn_decode_ex"]
 
 
 class CCAError(RuntimeError):
@@ -48,10 +49,12 @@ def load() -> ctypes.CDLL:
         "cca_last_error": ([], ctypes.c_char_p),
         "cca_visibility_table": ([I, I, I, P, P, P, P], I),
         "cca_pool_core": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, P], I),
+        "cca_pool_core_ex": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, P], I),
         "cca_attn_prefill": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, P], I),
         "cca_attn_prefill_ex": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, I, I, P], I),
         "cca_decode_workspace_bytes": ([I, I, I, I, I, I, I], S),
         "cca_attn_decode": ([P, P, P, P, P, I, P, P, I, P, I, P, I, P, S, I, I, I, I, I, I, I, P], I),
+        "cca_attn_decode_ex": ([P, P, P, P, P, I, P, P, I, P, I, P, I, P, S, I, I, I, I, I, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -105,13 +108,15 @@ def cca_visibility_table(L: int, g: int, w: int, n_core: torch.Tensor, win_lo: t
                                        _stream(stream)))
 
 
-def cca_pool_core(q, k, v, core_k, core_v, g: int, weights=None, stream=None) -> None:
-    """q [B,Hq,L,d]; k, v [B,Hkv,L,d]; core_k, core_v [B,Hkv,m_cap,d]; weights fp32 [B,Hkv,L//g,g]."""
+def cca_pool_core(q, k, v, core_k, core_v, g: int, weights=None, mode: int = CCA_POOL_SOFTMAX,
+                  stream=None) -> None:
+    """q [B,Hq,L,d]; k, v [B,Hkv,L,d]; core_k, core_v [B,Hkv,m_cap,d]; weights fp32 [B,Hkv,L//g,g];
+    mode: one of the CCA_POOL_* rules (q gives the shapes; the mean and max rules do not read it)."""
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
     m_cap = core_k.shape[2] if core_k is not None else 0
-    _check(load().cca_pool_core(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
-                                _ptr(weights), B, Hq, Hkv, L, d, g, _dt(q), _stream(stream)))
+    _check(load().cca_pool_core_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
+                                   _ptr(weights), B, Hq, Hkv, L, d, g, _dt(k), mode, _stream(stream)))
 
 
 def cca_attn_prefill(q, k, v, core_k, core_v, out, g: int, w: int, kernel: int = 0,
@@ -130,15 +135,17 @@ def cca_decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, m_cap: int, g:
 
 
 def cca_attn_decode(q_t, k_t, v_t, ring_k, ring_v, core_k, core_v, pos, out, workspace, g: int,
-                    w: int, advance_pos: bool = False, stream=None) -> None:
+                    w: int, advance_pos: bool = False, pool_mode: int = CCA_POOL_SOFTMAX,
+                    stream=None) -> None:
     """q_t [B,Hq,d]; k_t, v_t [B,Hkv,d]; ring_* [B,Hkv,R,d]; core_* [B,Hkv,m_cap,d];
-    pos int32 [B]; out [B,Hq,d]; workspace uint8 of cca_decode_workspace_bytes bytes."""
+    pos int32 [B]; out [B,Hq,d]; workspace uint8 of cca_decode_workspace_bytes bytes;
+    pool_mode: the CCA_POOL_* rule for the core appended when a group completes."""
     B, Hq, d = q_t.shape
     Hkv = k_t.shape[1]
     R = ring_k.shape[2]
     m_cap = core_k.shape[2]
-    _check(load().cca_attn_decode(_ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(ring_k), _ptr(ring_v), R,
-                                  _ptr(core_k), _ptr(core_v), m_cap, _ptr(pos), int(advance_pos),
-                                  _ptr(out), _dt(out), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, g, w,
-                                  _dt(q_t), _stream(stream)))
+    _check(load().cca_attn_decode_ex(_ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(ring_k), _ptr(ring_v), R,
+                                     _ptr(core_k), _ptr(core_v), m_cap, _ptr(pos), int(advance_pos),
+                                     _ptr(out), _dt(out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, g,
+                                     w, _dt(q_t), pool_mode, _stream(stream)))

@@ -9,6 +9,7 @@
 
 #include "../../include/cca.h"
 #include "cca_device.hpp"
+#include "cca_pool_group.hpp"
 #include "cca_internal.hpp"
 
 namespace {
@@ -103,14 +104,31 @@ cca_status cca_visibility_table(int L, int g, int w, int32_t* n_core, int32_t* w
                   fn);
 }
 
-cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core_k, void* core_v,
-                         int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d, int g,
-                         cca_dtype dt, void* stream) {
-  const char* fn = "cca_pool_core";
+namespace {
+
+// Pooling rule: a known mode, and at most kPoolHeadsMaxG heads per kv head for
+// the per-head rule.
+cca_status check_pool_mode(const char* fn, int mode, int Hq, int Hkv) {
+  if (mode < CCA_POOL_SOFTMAX || mode > CCA_POOL_MAX)
+    return fail(CCA_ERR_INVALID_ARG, "%s: unknown pooling mode %d", fn, mode);
+  if (mode == CCA_POOL_SOFTMAX_HEADS && Hq / Hkv > cca::kPoolHeadsMaxG)
+    return fail(CCA_ERR_UNSUPPORTED, "%s: per-head pooling needs G <= %d (G=%d)", fn,
+                cca::kPoolHeadsMaxG, Hq / Hkv);
+  return CCA_OK;
+}
+
+cca_status pool_core(const char* fn, const void* q, const void* k, const void* v, void* core_k,
+                     void* core_v, int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d,
+                     int g, cca_dtype dt, int mode, void* stream) {
   if (L < 1 || g < 1) return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d must be >= 1", fn, L, g);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
   if (st != CCA_OK) return st;
-  REQUIRE_PTR(q);
+  st = check_pool_mode(fn, mode, Hq, Hkv);
+  if (st != CCA_OK) return st;
+  if (mode == CCA_POOL_MAX && weights != nullptr)
+    return fail(CCA_ERR_INVALID_ARG, "%s: max pooling has no weights (weights must be NULL)", fn);
+  const bool reads_q = mode == CCA_POOL_SOFTMAX || mode == CCA_POOL_SOFTMAX_HEADS;
+  if (reads_q) REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
   const int m = L / g;
@@ -124,9 +142,25 @@ cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core
   if (weights != nullptr && !aligned16(weights))
     return fail(CCA_ERR_INVALID_ARG, "%s: weights is not 16-byte aligned", fn);
   cca::Shape sh{B, Hq, Hkv, L, d, g, 1};
-  return from_hip(cca::launch_pool(q, k, v, core_k, core_v, m_cap, weights, sh, dt,
+  return from_hip(cca::launch_pool(q, k, v, core_k, core_v, m_cap, weights, sh, dt, mode,
                                    static_cast<hipStream_t>(stream)),
                   fn);
+}
+
+}  // namespace
+
+cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core_k, void* core_v,
+                         int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d, int g,
+                         cca_dtype dt, void* stream) {
+  return pool_core("cca_pool_core", q, k, v, core_k, core_v, m_cap, weights, B, Hq, Hkv, L, d, g,
+                   dt, CCA_POOL_SOFTMAX, stream);
+}
+
+cca_status cca_pool_core_ex(const void* q, const void* k, const void* v, void* core_k,
+                            void* core_v, int m_cap, float* weights, int B, int Hq, int Hkv, int L,
+                            int d, int g, cca_dtype dt, int mode, void* stream) {
+  return pool_core("cca_pool_core_ex", q, k, v, core_k, core_v, m_cap, weights, B, Hq, Hkv, L, d,
+                   g, dt, mode, stream);
 }
 
 cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, const void* core_k,
@@ -179,14 +213,17 @@ size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int 
   return cca::decode_plan(B, Hq, Hkv, d, m_cap, g, w).ws_bytes;
 }
 
-cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
-                           void* ring_v, int R, void* core_k, void* core_v, int m_cap,
-                           int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
-                           void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
-                           int g, int w, cca_dtype dt, void* stream) {
-  const char* fn = "cca_attn_decode";
+namespace {
+
+cca_status attn_decode(const char* fn, const void* q_t, const void* k_t, const void* v_t,
+                       void* ring_k, void* ring_v, int R, void* core_k, void* core_v, int m_cap,
+                       int32_t* pos, int advance_pos, void* out, cca_dtype out_dt, void* workspace,
+                       size_t workspace_bytes, int B, int Hq, int Hkv, int d, int g, int w,
+                       cca_dtype dt, int pool_mode, void* stream) {
   if (g < 1 || w < 1) return fail(CCA_ERR_INVALID_ARG, "%s: g=%d w=%d must be >= 1", fn, g, w);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_pool_mode(fn, pool_mode, Hq, Hkv);
   if (st != CCA_OK) return st;
   st = check_out_dt(fn, out_dt, dt);
   if (st != CCA_OK) return st;
@@ -216,9 +253,31 @@ cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, vo
   if (plan.ws_bytes > 0) REQUIRE_PTR(workspace);
   cca::Shape sh{B, Hq, Hkv, 0, d, g, w};
   return from_hip(cca::launch_decode(q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v, m_cap, pos,
-                                     advance_pos, out, out_dt, workspace, plan, sh, dt,
+                                     advance_pos, out, out_dt, workspace, plan, sh, dt, pool_mode,
                                      static_cast<hipStream_t>(stream)),
                   fn);
+}
+
+}  // namespace
+
+cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                           void* ring_v, int R, void* core_k, void* core_v, int m_cap,
+                           int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                           void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
+                           int g, int w, cca_dtype dt, void* stream) {
+  return attn_decode("cca_attn_decode", q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v, m_cap,
+                     pos, advance_pos, out, out_dt, workspace, workspace_bytes, B, Hq, Hkv, d, g, w,
+                     dt, CCA_POOL_SOFTMAX, stream);
+}
+
+cca_status cca_attn_decode_ex(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                              void* ring_v, int R, void* core_k, void* core_v, int m_cap,
+                              int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                              void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                              int d, int g, int w, cca_dtype dt, int pool_mode, void* stream) {
+  return attn_decode("cca_attn_decode_ex", q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v, m_cap,
+                     pos, advance_pos, out, out_dt, workspace, workspace_bytes, B, Hq, Hkv, d, g, w,
+                     dt, pool_mode, stream);
 }
 
 }  // extern "C"

@@ -19,6 +19,7 @@
 // HBM-bound: every visible K/V byte is read once per step.
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
+#include "cca_pool_group.hpp"
 
 namespace cca {
 namespace {
@@ -27,141 +28,49 @@ constexpr int kThreads = 256;
 constexpr int kBatch = 4;  // keys per lane group per iteration
 
 template <int DT>
-struct Slice;  // a lane's 16-byte slice of a row, as floats
-template <>
-struct Slice<0> {
-  static constexpr int N = 4;
-  static __device__ __forceinline__ void load(const void* p, float* x) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-  }
-  static __device__ __forceinline__ void store(void* p, const float* x) {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-  }
-};
-template <>
-struct Slice<1> {
-  static constexpr int N = 8;
-  static __device__ __forceinline__ void load(const void* p, float* x) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-  static __device__ __forceinline__ void store(void* p, const float* x) {
-    uint4 v;
-    v.x = pack_bf16x2(x[0], x[1]);
-    v.y = pack_bf16x2(x[2], x[3]);
-    v.z = pack_bf16x2(x[4], x[5]);
-    v.w = pack_bf16x2(x[6], x[7]);
-    *reinterpret_cast<uint4*>(p) = v;
-  }
-};
+using Slice = Row16<DT>;  // a lane's 16-byte slice of a row, as floats
 
 __device__ __forceinline__ bool decode_valid(int t, int g, int m_cap) {
   return t >= 0 && (t + 1) / g <= m_cap;
 }
 
-// Pools the group ending at t with one wave: rows t-g+1..t-1 from the ring,
-// row t from k_t/v_t; pooling query = mean of q_t over the kv head's G heads.
+// Pools the group ending at t with one wave, in pooling mode `mode`: rows
+// t-g+1..t-1 from the ring, row t from k_t/v_t; the pooling queries are q_t of
+// the kv head's G heads (q_t points at the first of them).
 template <int DT, int D>
-__device__ void pool_new_group(const char* q_t, const char* k_new, const char* v_new,
-                               const char* ring_k, const char* ring_v, char* ck, char* cv, int t,
-                               int R, int g, int G, float scale_log2) {
-  typedef Slice<DT> S;
-  constexpr int ES = DT == 0 ? 4 : 2;
-  constexpr int EPL = S::N;
-  constexpr int LPK = D * ES / 16;
-  constexpr int KPW = 64 / LPK;
+__device__ __forceinline__ void pool_new_group(int mode, const char* q_t, const char* k_new,
+                                               const char* v_new, const char* ring_k,
+                                               const char* ring_v, char* ck, char* cv, int t,
+                                               int R, int g, int G, float scale_log2) {
+  typedef RowLanes<DT, D> RL;
+  auto krow = [&](int tau) {
+    const int p = t - g + 1 + tau;
+    return p == t ? k_new : ring_k + (long)(p % R) * D * RL::ES;
+  };
+  auto vrow = [&](int tau) {
+    const int p = t - g + 1 + tau;
+    return p == t ? v_new : ring_v + (long)(p % R) * D * RL::ES;
+  };
+  auto qrow = [&](int h) { return q_t + (long)h * D * RL::ES; };
+  float acck[RL::EPL], accv[RL::EPL];
+  switch (mode) {
+    case kPoolSoftmaxHeads:
+      pool_group<DT, D, kPoolSoftmaxHeads>(krow, vrow, qrow, g, G, scale_log2, acck, accv, nullptr);
+      break;
+    case kPoolMean:
+      pool_group<DT, D, kPoolMean>(krow, vrow, qrow, g, G, scale_log2, acck, accv, nullptr);
+      break;
+    case kPoolMax:
+      pool_group<DT, D, kPoolMax>(krow, vrow, qrow, g, G, scale_log2, acck, accv, nullptr);
+      break;
+    default:
+      pool_group<DT, D, kPoolSoftmax>(krow, vrow, qrow, g, G, scale_log2, acck, accv, nullptr);
+      break;
+  }
   const int lane = threadIdx.x & 63;
-  const int ks = lane / LPK;
-  const int d0 = (lane % LPK) * EPL;
-
-  float qbar[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) qbar[e] = 0.f;
-  for (int gh = 0; gh < G; ++gh) {
-    float x[EPL];
-    S::load(q_t + ((long)gh * D + d0) * ES, x);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qbar[e] += x[e];
-  }
-  const float invG = 1.0f / (float)G;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) qbar[e] *= invG;
-
-  float mrun = -INFINITY, lrun = 0.f, acck[EPL], accv[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acck[e] = accv[e] = 0.f;
-  for (int c0 = 0; c0 < g; c0 += KPW) {
-    const int tau = c0 + ks;
-    const bool valid = tau < g;
-    float kx[EPL], vx[EPL];
-    if (valid) {
-      const int p = t - g + 1 + tau;
-      const char* kr;
-      const char* vr;
-      if (p == t) {
-        kr = k_new;
-        vr = v_new;
-      } else {
-        kr = ring_k + (long)(p % R) * D * ES;
-        vr = ring_v + (long)(p % R) * D * ES;
-      }
-      S::load(kr + d0 * ES, kx);
-      S::load(vr + d0 * ES, vx);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) kx[e] = vx[e] = 0.f;
-    }
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) part = fmaf(qbar[e], kx[e], part);
-#pragma unroll
-    for (int o = LPK / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-    const float s = valid ? part * scale_log2 : -INFINITY;
-    const float mnew = fmaxf(mrun, s);
-    if (mnew != -INFINITY) {
-      const float alpha = exp2f(mrun - mnew);
-      const float pw = exp2f(s - mnew);
-      lrun = lrun * alpha + pw;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        acck[e] = fmaf(pw, kx[e], acck[e] * alpha);
-        accv[e] = fmaf(pw, vx[e], accv[e] * alpha);
-      }
-      mrun = mnew;
-    }
-  }
-#pragma unroll
-  for (int o = LPK; o < 64; o <<= 1) {
-    const float mo = __shfl_xor(mrun, o, 64);
-    const float lo = __shfl_xor(lrun, o, 64);
-    const float mnew = fmaxf(mrun, mo);
-    const float fa = mrun == -INFINITY ? 0.f : exp2f(mrun - mnew);
-    const float fb = mo == -INFINITY ? 0.f : exp2f(mo - mnew);
-    lrun = lrun * fa + lo * fb;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float ko = __shfl_xor(acck[e], o, 64);
-      const float vo = __shfl_xor(accv[e], o, 64);
-      acck[e] = acck[e] * fa + ko * fb;
-      accv[e] = accv[e] * fa + vo * fb;
-    }
-    mrun = mnew;
-  }
-  if (ks == 0) {
-    const float inv = 1.0f / lrun;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      acck[e] *= inv;
-      accv[e] *= inv;
-    }
-    S::store(ck + d0 * ES, acck);
-    S::store(cv + d0 * ES, accv);
+  if (lane < RL::LPK) {
+    Row16<DT>::store(ck + lane * RL::EPL * RL::ES, acck);
+    Row16<DT>::store(cv + lane * RL::EPL * RL::ES, accv);
   }
 }
 
@@ -172,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     void* __restrict__ ring_k_, void* __restrict__ ring_v_, int R, void* __restrict__ ck_,
     void* __restrict__ cv_, int m_cap, const int32_t* __restrict__ pos, float* __restrict__ ws_m,
     float* __restrict__ ws_l, float* __restrict__ ws_o, int Hq, int Hkv, int g, int w, int splits,
-    float scale_log2) {
+    float scale_log2, int pool_mode) {
   typedef Slice<DT> S;
   constexpr int ES = DT == 0 ? 4 : 2;
   constexpr int EPL = S::N;
@@ -218,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       }
     } else if (wave == 1 && (t + 1) % g == 0) {
       const int jn = (t + 1) / g - 1;
-      pool_new_group<DT, D>(q_t + ((long)b * Hq + (long)hk * G) * D * ES, k_new, v_new, ring_k,
+      pool_new_group<DT, D>(pool_mode, q_t + ((long)b * Hq + (long)hk * G) * D * ES, k_new, v_new, ring_k,
                             ring_v, ck + (long)jn * D * ES, cv + (long)jn * D * ES, t, R, g, G,
                             scale_log2);
     }
@@ -383,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
     const uint16_t* __restrict__ v_t, uint16_t* __restrict__ ring_k, uint16_t* __restrict__ ring_v,
     int R, uint16_t* __restrict__ ck, uint16_t* __restrict__ cv, int m_cap,
     const int32_t* __restrict__ pos, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    float* __restrict__ ws_o, int Hq, int Hkv, int g, int w, int splits, float c) {
+    float* __restrict__ ws_o, int Hq, int Hkv, int g, int w, int splits, float c, int pool_mode) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef float f32x16 __attribute__((ext_vector_type(16)));
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -430,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
       }
     } else if (wave == 1 && (t + 1) % g == 0) {
       const int jn = (t + 1) / g - 1;
-      pool_new_group<1, D>(reinterpret_cast<const char*>(q_t + ((long)b * Hq + h0) * D),
+      pool_new_group<1, D>(pool_mode, reinterpret_cast<const char*>(q_t + ((long)b * Hq + h0) * D),
                            reinterpret_cast<const char*>(k_new), reinterpret_cast<const char*>(v_new),
                            reinterpret_cast<const char*>(rk), reinterpret_cast<const char*>(rv),
                            reinterpret_cast<char*>(ckb + (long)jn * D), reinterpret_cast<char*>(cvb + (long)jn * D),
@@ -670,24 +579,25 @@ int pick_gt(int G) {
 template <int DT, int D, int GT>
 void launch_split(const void* q_t, const void* k_t, const void* v_t, void* ring_k, void* ring_v,
                   int R, void* ck, void* cv, int m_cap, const int32_t* pos, float* ws_m,
-                  float* ws_l, float* ws_o, const Shape& sh, int splits, hipStream_t s) {
+                  float* ws_l, float* ws_o, const Shape& sh, int splits, int pool_mode,
+                  hipStream_t s) {
   dim3 grid(splits, sh.Hq / GT, sh.B);
   const float scale_log2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((decode_split_kernel<DT, D, GT>), grid, dim3(kThreads), 0, s, q_t, k_t, v_t,
                      ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh.Hq, sh.Hkv, sh.g,
-                     sh.w, splits, scale_log2);
+                     sh.w, splits, scale_log2, pool_mode);
 }
 
 template <int DT, int D>
 void launch_split_g(int GT, const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                     void* ring_v, int R, void* ck, void* cv, int m_cap, const int32_t* pos,
                     float* ws_m, float* ws_l, float* ws_o, const Shape& sh, int splits,
-                    hipStream_t s) {
+                    int pool_mode, hipStream_t s) {
   switch (GT) {
-    case 8: launch_split<DT, D, 8>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, s); break;
-    case 4: launch_split<DT, D, 4>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, s); break;
-    case 2: launch_split<DT, D, 2>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, s); break;
-    default: launch_split<DT, D, 1>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, s); break;
+    case 8: launch_split<DT, D, 8>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, pool_mode, s); break;
+    case 4: launch_split<DT, D, 4>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, pool_mode, s); break;
+    case 2: launch_split<DT, D, 2>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, pool_mode, s); break;
+    default: launch_split<DT, D, 1>(q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, splits, pool_mode, s); break;
   }
 }
 
@@ -714,7 +624,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int m_cap, int g, int w) {
 hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                          void* ring_v, int R, void* ck, void* cv, int m_cap, int32_t* pos,
                          int advance_pos, void* out, int out_dt, void* ws, const DecodePlan& plan,
-                         const Shape& sh, int dt, hipStream_t s) {
+                         const Shape& sh, int dt, int pool_mode, hipStream_t s) {
   const int S = plan.splits;
   float* ws_m = static_cast<float*>(ws);
   float* ws_l = ws_m + (size_t)sh.B * sh.Hq * S;
@@ -731,15 +641,15 @@ hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void
     uint16_t* ck16 = static_cast<uint16_t*>(ck);
     uint16_t* cv16 = static_cast<uint16_t*>(cv);
     if (sh.d == 64)
-      hipLaunchKernelGGL((decode_mfma_kernel<64>), grid, dim3(256), 0, s, q16, k16, v16, rk16, rv16, R, ck16, cv16, m_cap, pos, ws_m, ws_l, ws_o, sh.Hq, sh.Hkv, sh.g, sh.w, S, c);
+      hipLaunchKernelGGL((decode_mfma_kernel<64>), grid, dim3(256), 0, s, q16, k16, v16, rk16, rv16, R, ck16, cv16, m_cap, pos, ws_m, ws_l, ws_o, sh.Hq, sh.Hkv, sh.g, sh.w, S, c, pool_mode);
     else
-      hipLaunchKernelGGL((decode_mfma_kernel<128>), grid, dim3(256), 0, s, q16, k16, v16, rk16, rv16, R, ck16, cv16, m_cap, pos, ws_m, ws_l, ws_o, sh.Hq, sh.Hkv, sh.g, sh.w, S, c);
+      hipLaunchKernelGGL((decode_mfma_kernel<128>), grid, dim3(256), 0, s, q16, k16, v16, rk16, rv16, R, ck16, cv16, m_cap, pos, ws_m, ws_l, ws_o, sh.Hq, sh.Hkv, sh.g, sh.w, S, c, pool_mode);
   } else if (dt == 0) {
-    if (sh.d == 64) launch_split_g<0, 64>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
-    else launch_split_g<0, 128>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
+    if (sh.d == 64) launch_split_g<0, 64>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, pool_mode, s);
+    else launch_split_g<0, 128>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, pool_mode, s);
   } else {
-    if (sh.d == 64) launch_split_g<1, 64>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
-    else launch_split_g<1, 128>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, s);
+    if (sh.d == 64) launch_split_g<1, 64>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, pool_mode, s);
+    else launch_split_g<1, 128>(GT, q_t, k_t, v_t, ring_k, ring_v, R, ck, cv, m_cap, pos, ws_m, ws_l, ws_o, sh, S, pool_mode, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

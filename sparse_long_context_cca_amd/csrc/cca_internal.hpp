@@ -17,8 +17,9 @@ struct Shape {
 hipError_t launch_visibility(int L, int g, int w, int32_t* n_core, int32_t* win_lo,
                              int32_t* group_last, hipStream_t s);
 
+// mode: PoolMode (cca_pool_group.hpp), equal to the cca_pool_mode values.
 hipError_t launch_pool(const void* q, const void* k, const void* v, void* ck, void* cv, int m_cap,
-                       float* weights, const Shape& sh, int dt, hipStream_t s);
+                       float* weights, const Shape& sh, int dt, int mode, hipStream_t s);
 
 // Vector-ALU prefill (fp32 math, any input dtype).
 hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, const void* ck,
@@ -39,6 +40,6 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int m_cap, int g, int w);
 hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                          void* ring_v, int R, void* ck, void* cv, int m_cap, int32_t* pos,
                          int advance_pos, void* out, int out_dt, void* ws, const DecodePlan& plan,
-                         const Shape& sh, int dt, hipStream_t s);
+                         const Shape& sh, int dt, int pool_mode, hipStream_t s);
 
 }  // namespace cca

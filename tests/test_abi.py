@@ -100,6 +100,44 @@ def test_decode_validation(cca_lib, kw, code):
     assert decode(cca_lib, **kw) == code
 
 
+def pool_ex(lib, mode, q=FAKE, k=FAKE, v=FAKE, ck=FAKE, cv=FAKE, m_cap=64, wts=None, B=1, Hq=4, Hkv=2,
+            L=1024, d=128, g=16, dt=1):
+    return lib.cca_pool_core_ex(P(q), P(k), P(v), P(ck), P(cv), m_cap, P(wts), B, Hq, Hkv, L, d, g, dt,
+                                mode, None)
+
+
+def decode_ex(lib, mode, **kw):
+    a = dict(q=FAKE, kt=FAKE, vt=FAKE, rk=FAKE, rv=FAKE, R=1024, ck=FAKE, cv=FAKE, m_cap=4096, pos=FAKE,
+             adv=0, out=FAKE, out_dt=1, ws=FAKE, ws_bytes=1 << 30, B=2, Hq=8, Hkv=2, d=128, g=16, w=1024,
+             dt=1)
+    a.update(kw)
+    return lib.cca_attn_decode_ex(P(a["q"]), P(a["kt"]), P(a["vt"]), P(a["rk"]), P(a["rv"]), a["R"],
+                                  P(a["ck"]), P(a["cv"]), a["m_cap"], P(a["pos"]), a["adv"], P(a["out"]),
+                                  a["out_dt"], P(a["ws"]), a["ws_bytes"], a["B"], a["Hq"], a["Hkv"],
+                                  a["d"], a["g"], a["w"], a["dt"], mode, None)
+
+
+@pytest.mark.parametrize("mode,kw,code", [
+    (-1, {}, INV), (4, {}, INV),                               # unknown rule
+    (_lib.CCA_POOL_MAX, dict(wts=FAKE), INV),                  # max pooling has no weights
+    (_lib.CCA_POOL_SOFTMAX_HEADS, dict(Hq=18, Hkv=2), UNS),    # per-head rule needs G <= 8
+    (_lib.CCA_POOL_SOFTMAX, dict(q=None), INV),                # the softmax rules read q
+    (_lib.CCA_POOL_SOFTMAX_HEADS, dict(q=None), INV),
+    (_lib.CCA_POOL_MEAN, dict(q=None, L=15, ck=None, cv=None, m_cap=0), OK),  # q unread, nothing to pool
+    (_lib.CCA_POOL_MAX, dict(q=None, m_cap=63), CAP),          # q unread: the next check speaks
+])
+def test_pool_mode_validation(cca_lib, mode, kw, code):
+    assert pool_ex(cca_lib, mode, **kw) == code
+
+
+@pytest.mark.parametrize("mode,kw,code", [
+    (-1, {}, INV), (9, {}, INV), (_lib.CCA_POOL_SOFTMAX_HEADS, dict(Hq=18, Hkv=2), UNS),
+    (_lib.CCA_POOL_MAX, dict(R=1023), CAP),
+])
+def test_decode_mode_validation(cca_lib, mode, kw, code):
+    assert decode_ex(cca_lib, mode, **kw) == code
+
+
 def test_decode_workspace_size(cca_lib):
     f = cca_lib.cca_decode_workspace_bytes
     n = f(8, 32, 8, 128, 4112, 16, 1024)

@@ -46,7 +46,11 @@ def cfg_of(name, B, Hq, Hkv, L, d, g, w, dt, seed=90, spiky=False, steps=0, scal
                                   decode_steps=steps)
 
 
-def gpu_pool(q, k, v, g, m_cap=None, weights=False):
+MODES = {cca.CCA_POOL_SOFTMAX: "softmax", cca.CCA_POOL_SOFTMAX_HEADS: "softmax_heads",
+         cca.CCA_POOL_MEAN: "mean", cca.CCA_POOL_MAX: "max"}
+
+
+def gpu_pool(q, k, v, g, m_cap=None, weights=False, mode=cca.CCA_POOL_SOFTMAX):
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
     m = L // g
@@ -54,8 +58,20 @@ def gpu_pool(q, k, v, g, m_cap=None, weights=False):
     ck = torch.full((B, Hkv, m_cap, d), float("nan"), dtype=q.dtype, device=DEV)
     cv = torch.full_like(ck, float("nan"))
     wt = torch.full((B, Hkv, max(m, 1), g), float("nan"), dtype=torch.float32, device=DEV) if weights else None
-    cca.cca_pool_core(q, k, v, ck, cv, g, weights=wt)
+    cca.cca_pool_core(q, k, v, ck, cv, g, weights=wt, mode=mode)
     return ck, cv, wt
+
+
+def check_cores(dt, got, ref, mode):
+    """Pooled cores against the oracle: max pooling selects stored values, so
+    it is exact; the other rules round once to the storage dtype."""
+    if mode == cca.CCA_POOL_MAX:
+        assert np.array_equal(host(got), ref)
+    elif dt == "f32":
+        assert err(got, ref) <= 1e-5
+    else:
+        bound = np.abs(ref) * 2.0 ** -8 * 1.01 + 1e-6
+        assert np.all(np.abs(host(got) - ref) <= bound)
 
 
 # ------------------------------------------------------------- index tables
@@ -106,6 +122,27 @@ def test_pool_parity(dt, case):
             assert np.all(np.abs(host(got) - ref) <= bound)
     assert err(wt[:, :, :m], A) <= 1e-5
     assert float((wt[:, :, :m].sum(-1) - 1).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("mode", [cca.CCA_POOL_SOFTMAX_HEADS, cca.CCA_POOL_MEAN, cca.CCA_POOL_MAX],
+                         ids=lambda m: MODES[m])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("case", [POOL_CASES[i] for i in (1, 2, 3, 4, 6)], ids=lambda c: "x".join(map(str, c)))
+def test_pool_modes_parity(mode, dt, case):
+    B, Hq, Hkv, L, d, g = case
+    say(f"pool mode {MODES[mode]} {dt} B={B} Hq={Hq} Hkv={Hkv} L={L} d={d} g={g}")
+    cfg = cfg_of("poolm", B, Hq, Hkv, L, d, g, 1, dt, seed=41 + L)
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    want_w = mode != cca.CCA_POOL_MAX
+    ck, cv, wt = gpu_pool(q.to(DEV), k.to(DEV), v.to(DEV), g, m_cap=L // g + 2, weights=want_w, mode=mode)
+    torch.cuda.synchronize()
+    CK, CV, A = orc.pool_core(f32np(q), f32np(k), f32np(v), g, MODES[mode])
+    m = L // g
+    assert torch.isnan(ck[:, :, m:]).all(), "slots beyond L/g must be untouched"
+    check_cores(dt, ck[:, :, :m], CK, mode)
+    check_cores(dt, cv[:, :, :m], CV, mode)
+    if want_w:
+        assert err(wt[:, :, :m], A) <= 1e-5
 
 
 def test_pool_is_deterministic():
@@ -231,21 +268,22 @@ def test_prefill_full_size_sampled(number):
 # ------------------------------------------------------------------- decode
 
 
-def decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed, advance=True):
+def decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed, advance=True,
+               mode=cca.CCA_POOL_SOFTMAX):
     """Decode `steps` tokens per sequence from caches built on the GPU (pool
     kernel over the shared history + ring fill), checking every step."""
     T = max(pos0) + steps
     cfg = cfg_of("dec", B, Hq, Hkv, T, d, g, w, dt, seed=seed, scale=1.0 if dt == "bf16" else d ** -0.5)
     q, k, v = cca_inputs.prefill_inputs(cfg)
     Q, K, V = f32np(q), f32np(k), f32np(v)
-    CK, CV, _ = orc.pool_core(Q, K, V, g)
+    CK, CV, _ = orc.pool_core(Q, K, V, g, MODES[mode])
     Lh = max(pos0)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     ck = torch.zeros((B, Hkv, m_cap, d), dtype=q.dtype, device=DEV)
     cv = torch.zeros_like(ck)
     if Lh // g:
         ck_h, cv_h, _ = gpu_pool(qd[:, :, :Lh].contiguous(), kd[:, :, :Lh].contiguous(),
-                                 vd[:, :, :Lh].contiguous(), g)
+                                 vd[:, :, :Lh].contiguous(), g, mode=mode)
         n = min(m_cap, Lh // g)
         ck[:, :, :n] = ck_h[:, :, :n]
         cv[:, :, :n] = cv_h[:, :, :n]
@@ -267,7 +305,8 @@ def decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed, advance=Tru
         v_t = vd[bidx, :, t].contiguous()
         if not advance:
             pos.copy_(t.to(torch.int32))
-        cca.cca_attn_decode(q_t, k_t, v_t, rk, rv, ck, cv, pos, out, ws, g, w, advance_pos=advance)
+        cca.cca_attn_decode(q_t, k_t, v_t, rk, rv, ck, cv, pos, out, ws, g, w, advance_pos=advance,
+                            pool_mode=mode)
         torch.cuda.synchronize()
         tt = np.array([p + i for p in pos0])
         ref = orc.attn_decode(Q[np.arange(B), :, tt], K, V, CK, CV, tt, g, w)
@@ -282,12 +321,8 @@ def decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed, advance=Tru
             assert torch.equal(rk[b, :, p % R], kd[b, :, p]) and torch.equal(rv[b, :, p % R], vd[b, :, p])
         nj = min(tl // g, m_cap)
         if nj:
-            tol = 1e-5 if dt == "f32" else None
-            got, ref = host(ck[b, :, :nj]), CK[b, :, :nj]
-            if tol:
-                assert np.abs(got - ref).max() <= tol
-            else:
-                assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 * 1.01 + 1e-6)
+            check_cores(dt, ck[b, :, :nj], CK[b, :, :nj], mode)
+            check_cores(dt, cv[b, :, :nj], CV[b, :, :nj], mode)
     return worst
 
 
@@ -306,6 +341,21 @@ def test_decode_parity(case):
     dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap = case
     say(f"decode {case}")
     worst = decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed=300 + d + B)
+    say(f"  max abs err over steps {worst:.3e}")
+    assert worst <= TOL[dt]
+
+
+@pytest.mark.parametrize("mode", [cca.CCA_POOL_SOFTMAX_HEADS, cca.CCA_POOL_MEAN, cca.CCA_POOL_MAX],
+                         ids=lambda m: MODES[m])
+@pytest.mark.parametrize("case", [DECODE_CASES[i] for i in (0, 1, 3)],
+                         ids=lambda c: f"{c[0]}-d{c[1]}-B{c[2]}-G{c[3] // c[4]}-g{c[5]}-w{c[6]}")
+def test_decode_pool_modes(mode, case):
+    """Decode continuing a cache pooled with another rule: the cores appended
+    on group completion follow the same rule, and every step matches the
+    oracle pooled that way."""
+    dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap = case
+    say(f"decode pool mode {MODES[mode]} {case}")
+    worst = decode_run(dt, d, B, Hq, Hkv, g, w, R, pos0, steps, m_cap, seed=500 + d + B, mode=mode)
     say(f"  max abs err over steps {worst:.3e}")
     assert worst <= TOL[dt]
 
