@@ -157,6 +157,61 @@ cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, cons
                                int kernel, void* stream);
 
 /*
+ * Chunked and variable-length prefill.  The article notes that CCA generates
+ * with token counts that are not multiples of g; a long prompt is processed in
+ * chunks, and sequences of one batch have their own lengths.  Each sequence b
+ * covers the query positions q_start[b] .. q_start[b] + q_len[b] - 1 (q_start,
+ * q_len: device int32 [B], 4-byte aligned; q_len[b] may be 0), stored at local
+ * rows 0 .. q_len[b]-1 of q and out ([B,Hq,Lq,d], rows >= q_len[b] untouched);
+ * its k/v ([B,Hkv,Lk,d]) hold positions 0 .. q_start[b] + q_len[b] - 1 (the
+ * cached prefix and the chunk).  A chunked pass is the same computation as one
+ * full prefill: chunk after chunk, cca_pool_core_chunk then
+ * cca_attn_prefill_chunk give exactly the rows cca_pool_core + cca_attn_prefill
+ * give over the whole sequence (up to summation order).  A sequence whose
+ * range does not fit (q_start < 0, q_len < 0 or > Lq, q_start + q_len > Lk,
+ * or a visible core beyond m_cap) gets NaN in its Lq output rows and no cache
+ * writes; the arrays live on the device, so this is not a status.
+ *
+ * cca_pool_core_chunk - pools, with rule `mode`, every group j < m_cap whose
+ *   last token (j+1)g-1 lies among the covered positions of its sequence; the
+ *   pooling query is that row of q (groups may start before q_start: their
+ *   tokens come from k/v).  Writes core slots j of core_k/core_v
+ *   ([B,Hkv,m_cap,d]).  q is not read by CCA_POOL_MEAN / CCA_POOL_MAX.
+ */
+cca_status cca_pool_core_chunk(const void* q, const void* k, const void* v, void* core_k,
+                               void* core_v, int m_cap, const int32_t* q_start,
+                               const int32_t* q_len, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                               int g, cca_dtype dt, int mode, void* stream);
+
+/*
+ * cca_attn_prefill_chunk - the fused attention rows of the covered positions
+ *   (digest, "Method", fusion formula), each row t over cores 0 .. n_core(t)-1
+ *   (core_k/core_v [B,Hkv,m_cap,d], pooled by earlier chunk calls) and raw
+ *   positions win_lo(t) .. t of k/v.  out [B,Hq,Lq,d] in out_dt.  bf16 inputs
+ *   run on the matrix cores, fp32 inputs on the vector ALUs.
+ * Errors: INVALID_ARG (null or misaligned pointers, Lq or Lk < 1, g or w < 1,
+ *   m_cap < 0), UNSUPPORTED as cca_attn_prefill.
+ */
+cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, const void* core_k,
+                                  const void* core_v, int m_cap, void* out, cca_dtype out_dt,
+                                  const int32_t* q_start, const int32_t* q_len, int B, int Hq,
+                                  int Hkv, int Lq, int Lk, int d, int g, int w, cca_dtype dt,
+                                  void* stream);
+
+/*
+ * cca_cache_fill_ring - prefill -> decode handoff: copies positions
+ *   max(0, len-R) .. len-1 of k/v ([B,Hkv,Lk,d]), len = seq_len[b] (device
+ *   int32 [B]), into ring slot p % R of ring_k/ring_v ([B,Hkv,R,d]).  With the
+ *   cores pooled up to len and pos[b] = len, cca_attn_decode then continues
+ *   the sequence.  A len outside 0 .. Lk copies nothing.
+ * Errors: INVALID_ARG (null or misaligned pointers, R or Lk < 1), UNSUPPORTED
+ *   (d, dt, B*Hkv > 65535).
+ */
+cca_status cca_cache_fill_ring(const void* k, const void* v, void* ring_k, void* ring_v, int R,
+                               const int32_t* seq_len, int B, int Hkv, int Lk, int d, cca_dtype dt,
+                               void* stream);
+
+/*
  * cca_decode_workspace_bytes - size of the workspace cca_attn_decode needs for
  * these shapes (fp32 partial softmax states of its split-K pass).
  */

@@ -21,7 +21,8 @@ CCA_POOL_SOFTMAX, CCA_POOL_SOFTMAX_HEADS, CCA_POOL_MEAN, CCA_POOL_MAX = range(4)
 
 EXPORTS = ["cca_version", "cca_status_string", "cca_last_error", "cca_visibility_table",
            "cca_pool_core", "cca_pool_core_ex", "cca_attn_prefill", "cca_attn_prefill_ex",
-           "cca_decode_workspace_bytes", "cca_attn_decode", "cca_attn_decode_ex"]
+           "cca_decode_workspace_bytes", "cca_attn_decode", "cca_attn_decode_ex",
+           "cca_pool_core_chunk", "cca_attn_prefill_chunk", "cca_cache_fill_ring"]
 
 
 class CCAError(RuntimeError):
@@ -55,6 +56,9 @@ def load() -> ctypes.CDLL:
         "cca_decode_workspace_bytes": ([I, I, I, I, I, I, I], S),
         "cca_attn_decode": ([P, P, P, P, P, I, P, P, I, P, I, P, I, P, S, I, I, I, I, I, I, I, P], I),
         "cca_attn_decode_ex": ([P, P, P, P, P, I, P, P, I, P, I, P, I, P, S, I, I, I, I, I, I, I, I, P], I),
+        "cca_pool_core_chunk": ([P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, P], I),
+        "cca_attn_prefill_chunk": ([P, P, P, P, P, I, P, I, P, P, I, I, I, I, I, I, I, I, I, P], I),
+        "cca_cache_fill_ring": ([P, P, P, P, I, P, I, I, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -149,3 +153,43 @@ def cca_attn_decode(q_t, k_t, v_t, ring_k, ring_v, core_k, core_v, pos, out, wor
                                      _ptr(out), _dt(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, g,
                                      w, _dt(q_t), pool_mode, _stream(stream)))
+
+
+def _rows(t):
+    if t is None or t.dtype != torch.int32:
+        raise CCAError(CCA_ERR_INVALID_ARG, "q_start / q_len / seq_len must be int32 device tensors")
+    return _ptr(t)
+
+
+def cca_pool_core_chunk(q, k, v, core_k, core_v, g: int, q_start, q_len,
+                        mode: int = CCA_POOL_SOFTMAX, stream=None) -> None:
+    """Pools the groups completed by each sequence's chunk.  q [B,Hq,Lq,d] holds the chunk rows
+    (local row i = position q_start[b] + i); k, v [B,Hkv,Lk,d] hold positions 0..; q_start, q_len
+    int32 [B] on the device; core_k, core_v [B,Hkv,m_cap,d]."""
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    m_cap = core_k.shape[2]
+    _check(load().cca_pool_core_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
+                                      _rows(q_start), _rows(q_len), B, Hq, Hkv, Lq, Lk, d, g, _dt(k),
+                                      mode, _stream(stream)))
+
+
+def cca_attn_prefill_chunk(q, k, v, core_k, core_v, out, g: int, w: int, q_start, q_len,
+                           stream=None) -> None:
+    """Fused attention rows of each sequence's chunk (see cca_pool_core_chunk for the layout);
+    out [B,Hq,Lq,d] in q's dtype or fp32."""
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    m_cap = core_k.shape[2] if core_k is not None else 0
+    _check(load().cca_attn_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
+                                         _ptr(out), _dt(out), _rows(q_start), _rows(q_len), B, Hq, Hkv,
+                                         Lq, Lk, d, g, w, _dt(q), _stream(stream)))
+
+
+def cca_cache_fill_ring(k, v, ring_k, ring_v, seq_len, stream=None) -> None:
+    """Copies the last R positions below seq_len[b] of k, v [B,Hkv,Lk,d] into ring slot p % R
+    of ring_k, ring_v [B,Hkv,R,d]."""
+    B, Hkv, Lk, d = k.shape
+    R = ring_k.shape[2]
+    _check(load().cca_cache_fill_ring(_ptr(k), _ptr(v), _ptr(ring_k), _ptr(ring_v), R, _rows(seq_len),
+                                      B, Hkv, Lk, d, _dt(k), _stream(stream)))

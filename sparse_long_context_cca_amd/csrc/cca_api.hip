@@ -142,9 +142,21 @@ cca_status pool_core(const char* fn, const void* q, const void* k, const void* v
   if (weights != nullptr && !aligned16(weights))
     return fail(CCA_ERR_INVALID_ARG, "%s: weights is not 16-byte aligned", fn);
   cca::Shape sh{B, Hq, Hkv, L, d, g, 1};
-  return from_hip(cca::launch_pool(q, k, v, core_k, core_v, m_cap, weights, sh, dt, mode,
+  cca::RowRange rr;
+  rr.Lq = rr.Lk = L;
+  return from_hip(cca::launch_pool(q, k, v, core_k, core_v, m_cap, weights, sh, rr, dt, mode,
                                    static_cast<hipStream_t>(stream)),
                   fn);
+}
+
+// Per-sequence row arrays of the chunked calls: device int32 [B], 4-byte aligned.
+cca_status check_rows(const char* fn, const int32_t* q_start, const int32_t* q_len, int Lq, int Lk) {
+  if (q_start == nullptr || q_len == nullptr)
+    return fail(CCA_ERR_INVALID_ARG, "%s: q_start and q_len must not be NULL", fn);
+  if ((reinterpret_cast<uintptr_t>(q_start) & 3u) != 0 || (reinterpret_cast<uintptr_t>(q_len) & 3u) != 0)
+    return fail(CCA_ERR_INVALID_ARG, "%s: q_start / q_len are not 4-byte aligned", fn);
+  if (Lq < 1 || Lk < 1) return fail(CCA_ERR_INVALID_ARG, "%s: Lq=%d Lk=%d must be >= 1", fn, Lq, Lk);
+  return CCA_OK;
 }
 
 }  // namespace
@@ -161,6 +173,39 @@ cca_status cca_pool_core_ex(const void* q, const void* k, const void* v, void* c
                             int d, int g, cca_dtype dt, int mode, void* stream) {
   return pool_core("cca_pool_core_ex", q, k, v, core_k, core_v, m_cap, weights, B, Hq, Hkv, L, d,
                    g, dt, mode, stream);
+}
+
+cca_status cca_pool_core_chunk(const void* q, const void* k, const void* v, void* core_k,
+                               void* core_v, int m_cap, const int32_t* q_start,
+                               const int32_t* q_len, int B, int Hq, int Hkv, int Lq, int Lk, int d,
+                               int g, cca_dtype dt, int mode, void* stream) {
+  const char* fn = "cca_pool_core_chunk";
+  if (g < 1) return fail(CCA_ERR_INVALID_ARG, "%s: g=%d must be >= 1", fn, g);
+  cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_pool_mode(fn, mode, Hq, Hkv);
+  if (st != CCA_OK) return st;
+  st = check_rows(fn, q_start, q_len, Lq, Lk);
+  if (st != CCA_OK) return st;
+  if (mode == CCA_POOL_SOFTMAX || mode == CCA_POOL_SOFTMAX_HEADS) REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  if (m_cap < 0) return fail(CCA_ERR_INVALID_ARG, "%s: m_cap=%d", fn, m_cap);
+  st = check_sizes(fn, (long long)B * Hq * Lq * d, (long long)B * Hkv * Lk * d,
+                   (long long)B * Hkv * m_cap * d);
+  if (st != CCA_OK) return st;
+  if (m_cap == 0) return ok();  // no core slot: nothing to write
+  REQUIRE_PTR(core_k);
+  REQUIRE_PTR(core_v);
+  cca::Shape sh{B, Hq, Hkv, Lq, d, g, 1};
+  cca::RowRange rr;
+  rr.q_start = q_start;
+  rr.q_len = q_len;
+  rr.Lq = Lq;
+  rr.Lk = Lk;
+  return from_hip(cca::launch_pool(q, k, v, core_k, core_v, m_cap, nullptr, sh, rr, dt, mode,
+                                   static_cast<hipStream_t>(stream)),
+                  fn);
 }
 
 cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, const void* core_k,
@@ -193,10 +238,74 @@ cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, cons
     return fail(CCA_ERR_UNSUPPORTED, "%s: the matrix-core kernel takes bf16 inputs", fn);
   if (kernel == 0) kernel = (dt == CCA_BF16) ? 2 : 1;
   cca::Shape sh{B, Hq, Hkv, L, d, g, w};
+  cca::RowRange rr;
+  rr.Lq = rr.Lk = L;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (kernel == 2)
-    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, s), fn);
-  return from_hip(cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, dt, s),
+    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, s),
+                    fn);
+  return from_hip(
+      cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, dt, s), fn);
+}
+
+cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, const void* core_k,
+                                  const void* core_v, int m_cap, void* out, cca_dtype out_dt,
+                                  const int32_t* q_start, const int32_t* q_len, int B, int Hq,
+                                  int Hkv, int Lq, int Lk, int d, int g, int w, cca_dtype dt,
+                                  void* stream) {
+  const char* fn = "cca_attn_prefill_chunk";
+  if (g < 1 || w < 1) return fail(CCA_ERR_INVALID_ARG, "%s: g=%d w=%d must be >= 1", fn, g, w);
+  cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_out_dt(fn, out_dt, dt);
+  if (st != CCA_OK) return st;
+  st = check_rows(fn, q_start, q_len, Lq, Lk);
+  if (st != CCA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  if (m_cap < 0) return fail(CCA_ERR_INVALID_ARG, "%s: m_cap=%d", fn, m_cap);
+  if (m_cap > 0) {
+    REQUIRE_PTR(core_k);
+    REQUIRE_PTR(core_v);
+  }
+  st = check_sizes(fn, (long long)B * Hq * Lq * d, (long long)B * Hkv * Lk * d,
+                   (long long)B * Hkv * m_cap * d);
+  if (st != CCA_OK) return st;
+  cca::Shape sh{B, Hq, Hkv, Lq, d, g, w};
+  cca::RowRange rr;
+  rr.q_start = q_start;
+  rr.q_len = q_len;
+  rr.Lq = Lq;
+  rr.Lk = Lk;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == CCA_BF16)
+    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, s),
+                    fn);
+  return from_hip(
+      cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, dt, s), fn);
+}
+
+cca_status cca_cache_fill_ring(const void* k, const void* v, void* ring_k, void* ring_v, int R,
+                               const int32_t* seq_len, int B, int Hkv, int Lk, int d, cca_dtype dt,
+                               void* stream) {
+  const char* fn = "cca_cache_fill_ring";
+  cca_status st = check_heads(fn, B, Hkv, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  if (R < 1 || Lk < 1) return fail(CCA_ERR_INVALID_ARG, "%s: R=%d Lk=%d must be >= 1", fn, R, Lk);
+  if (seq_len == nullptr || (reinterpret_cast<uintptr_t>(seq_len) & 3u) != 0)
+    return fail(CCA_ERR_INVALID_ARG, "%s: seq_len is NULL or not 4-byte aligned", fn);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(ring_k);
+  REQUIRE_PTR(ring_v);
+  st = check_sizes(fn, (long long)B * Hkv * Lk * d, (long long)B * Hkv * R * d, 0);
+  if (st != CCA_OK) return st;
+  if ((long long)B * Hkv > 65535)
+    return fail(CCA_ERR_UNSUPPORTED, "%s: B*Hkv=%lld exceeds 65535", fn, (long long)B * Hkv);
+  return from_hip(cca::launch_fill_ring(k, v, ring_k, ring_v, R, seq_len, B, Hkv, Lk, d,
+                                        dt == CCA_BF16 ? 2 : 4, static_cast<hipStream_t>(stream)),
                   fn);
 }
 

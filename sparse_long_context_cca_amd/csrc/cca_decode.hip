@@ -17,6 +17,8 @@
 //   pass 2 merges the split states per (b, query head), writes the output and
 //   optionally advances pos[b].
 // HBM-bound: every visible K/V byte is read once per step.
+#include <algorithm>
+
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
 #include "cca_pool_group.hpp"
@@ -601,7 +603,43 @@ void launch_split_g(int GT, const void* q_t, const void* k_t, const void* v_t, v
   }
 }
 
+// Prefill -> decode handoff: the last R positions of each sequence into its ring.
+__global__ __launch_bounds__(256) void fill_ring_kernel(const char* __restrict__ k,
+                                                        const char* __restrict__ v,
+                                                        char* __restrict__ ring_k,
+                                                        char* __restrict__ ring_v, int R,
+                                                        const int32_t* __restrict__ seq_len, int Hkv,
+                                                        int Lk, int row_bytes) {
+  const int bh = blockIdx.y;  // b * Hkv + kv head
+  const int len = seq_len[bh / Hkv];
+  if (len < 0 || len > Lk) return;
+  const int n = min(len, R);  // rows to copy: positions len-n .. len-1
+  const int cpr = row_bytes / 16;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < (long)n * cpr;
+       i += (long)gridDim.x * blockDim.x) {
+    const int r = (int)(i / cpr), c = (int)(i % cpr);
+    const int p = len - n + r;
+    const long src = ((long)bh * Lk + p) * row_bytes + c * 16;
+    const long dst = ((long)bh * R + p % R) * row_bytes + c * 16;
+    *reinterpret_cast<uint4*>(ring_k + dst) = *reinterpret_cast<const uint4*>(k + src);
+    *reinterpret_cast<uint4*>(ring_v + dst) = *reinterpret_cast<const uint4*>(v + src);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fill_ring(const void* k, const void* v, void* ring_k, void* ring_v, int R,
+                            const int32_t* seq_len, int B, int Hkv, int Lk, int d, int elem_bytes,
+                            hipStream_t s) {
+  const int row_bytes = d * elem_bytes;
+  const long chunks = (long)R * (row_bytes / 16);
+  const int bx = (int)std::min<long>((chunks + 255) / 256, 64);
+  hipLaunchKernelGGL(fill_ring_kernel, dim3(bx, B * Hkv), dim3(256), 0, s,
+                     static_cast<const char*>(k), static_cast<const char*>(v),
+                     static_cast<char*>(ring_k), static_cast<char*>(ring_v), R, seq_len, Hkv, Lk,
+                     row_bytes);
+  return hipGetLastError();
+}
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int m_cap, int g, int w) {
   (void)g;

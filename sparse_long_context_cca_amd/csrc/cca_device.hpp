@@ -25,6 +25,29 @@ __host__ __device__ __forceinline__ int n_core(int t, int g, int w) {
 
 __host__ __device__ __forceinline__ int group_last(int j, int g) { return (j + 1) * g - 1; }
 
+// Query rows of sequence b in a chunked / variable-length call (see RowRange):
+// q_start and q_len from device arrays, or 0 and Lq when there are none.  ok
+// is false when the range does not fit the buffers (q_start < 0, q_len < 0,
+// q_len > Lq, q_start + q_len > Lk) or sees a core beyond m_cap; such a
+// sequence gets NaN rows and nothing is read for it.
+struct SeqRows {
+  int qs, ql;
+  bool ok;
+};
+__device__ __forceinline__ SeqRows seq_rows(const int32_t* q_start, const int32_t* q_len, int b,
+                                            int Lq, int Lk, int g, int w, int m_cap) {
+  SeqRows r;
+  r.qs = 0;
+  r.ql = Lq;
+  if (q_start != nullptr) {
+    r.qs = __builtin_amdgcn_readfirstlane(q_start[b]);
+    r.ql = __builtin_amdgcn_readfirstlane(q_len[b]);
+  }
+  r.ok = r.qs >= 0 && r.ql >= 0 && r.ql <= Lq && (long)r.qs + r.ql <= Lk &&
+         (r.ql == 0 || n_core(r.qs + r.ql - 1, g, w) <= m_cap);
+  return r;
+}
+
 typedef uint16_t bf16_bits;
 
 // bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even via the

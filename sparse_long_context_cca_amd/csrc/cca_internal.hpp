@@ -14,22 +14,38 @@ struct Shape {
   int m() const { return L / g; }
 };
 
+// The query rows a prefill or pooling call covers.  Sequence b's rows are
+// positions q_start[b] .. q_start[b] + q_len[b] - 1, stored at local rows 0..
+// of Q and of the output (Lq rows per sequence); its K and V hold positions
+// 0 .. Lk - 1 (only those below q_start[b] + q_len[b] are read).  Null arrays
+// (both or neither) mean q_start = 0 and q_len = Lq: every row of a full
+// prefill, with Lq = Lk = L.
+struct RowRange {
+  const int32_t* q_start = nullptr;
+  const int32_t* q_len = nullptr;
+  int Lq = 0;
+  int Lk = 0;
+};
+
 hipError_t launch_visibility(int L, int g, int w, int32_t* n_core, int32_t* win_lo,
                              int32_t* group_last, hipStream_t s);
 
 // mode: PoolMode (cca_pool_group.hpp), equal to the cca_pool_mode values.
+// Pools the groups whose last token lies among the covered rows (all complete
+// groups of a full prefill); the pooling queries come from Q's local rows.
 hipError_t launch_pool(const void* q, const void* k, const void* v, void* ck, void* cv, int m_cap,
-                       float* weights, const Shape& sh, int dt, int mode, hipStream_t s);
+                       float* weights, const Shape& sh, const RowRange& rr, int dt, int mode,
+                       hipStream_t s);
 
 // Vector-ALU prefill (fp32 math, any input dtype).
 hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, const void* ck,
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
-                               int dt, hipStream_t s);
+                               const RowRange& rr, int dt, hipStream_t s);
 
 // bf16 matrix-core prefill.
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* ck,
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
-                               hipStream_t s);
+                               const RowRange& rr, hipStream_t s);
 
 struct DecodePlan {
   int splits;         // key-range splits per (b, kv head)
@@ -41,5 +57,11 @@ hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void
                          void* ring_v, int R, void* ck, void* cv, int m_cap, int32_t* pos,
                          int advance_pos, void* out, int out_dt, void* ws, const DecodePlan& plan,
                          const Shape& sh, int dt, int pool_mode, hipStream_t s);
+
+// Copies positions max(0, len-R) .. len-1 of sequence b's K and V (len =
+// seq_len[b], device) into ring slot p % R; a len outside 0 .. Lk copies nothing.
+hipError_t launch_fill_ring(const void* k, const void* v, void* ring_k, void* ring_v, int R,
+                            const int32_t* seq_len, int B, int Hkv, int Lk, int d, int elem_bytes,
+                            hipStream_t s);
 
 }  // namespace cca

@@ -46,27 +46,36 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q_,
                                                    const void* __restrict__ k_,
                                                    const void* __restrict__ v_,
                                                    void* __restrict__ ck_, void* __restrict__ cv_,
-                                                   float* __restrict__ weights, int m_cap, int B,
-                                                   int Hq, int Hkv, int L, int g, float scale_log2) {
+                                                   float* __restrict__ weights, int m_cap,
+                                                   const int32_t* __restrict__ q_start,
+                                                   const int32_t* __restrict__ q_len, int gpb,
+                                                   int B, int Hq, int Hkv, int Lq, int Lk, int g,
+                                                   float scale_log2) {
   typedef RowLanes<DT, D> RL;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int m = L / g;
-  const long group = (long)blockIdx.x * (blockDim.x >> 6) + wave;
-  if (group >= (long)B * Hkv * m) return;
-  const int j = (int)(group % m);
-  const long bh = group / m;  // b * Hkv + hk
+  // one wave per (b, kv head, group slot); gpb slots per (b, kv head)
+  const long slot = (long)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (slot >= (long)B * Hkv * gpb) return;
+  const int jl = (int)(slot % gpb);
+  const long bh = slot / gpb;  // b * Hkv + hk
   const int hk = (int)(bh % Hkv);
   const int b = (int)(bh / Hkv);
   const int G = Hq / Hkv;
+  // the groups whose last token lies among sequence b's rows qs .. qs+ql-1
+  const SeqRows sr = seq_rows(q_start, q_len, b, Lq, Lk, g, 1, 0x7fffffff);
+  if (!sr.ok) return;
+  const int j = (sr.qs + g) / g - 1 + jl;  // first such group, plus jl
+  if (j >= (sr.qs + sr.ql) / g || j >= m_cap) return;
+  const int m = Lq / g;  // weights rows per (b, kv head) (full prefill only)
   const char* qb = static_cast<const char*>(q_);
   const char* kb = static_cast<const char*>(k_);
   const char* vb = static_cast<const char*>(v_);
-  const long kv_row0 = (long)bh * L + (long)j * g;  // first token of the group
-  const int last = group_last(j, g);
+  const long kv_row0 = (long)bh * Lk + (long)j * g;  // first token of the group
+  const int last = group_last(j, g) - sr.qs;          // local row of its last token
   auto krow = [&](int tau) { return kb + (kv_row0 + tau) * D * RL::ES; };
   auto vrow = [&](int tau) { return vb + (kv_row0 + tau) * D * RL::ES; };
-  auto qrow = [&](int h) { return qb + ((long)(b * Hq + hk * G + h) * L + last) * D * RL::ES; };
+  auto qrow = [&](int h) { return qb + ((long)(b * Hq + hk * G + h) * Lq + last) * D * RL::ES; };
   float acck[RL::EPL], accv[RL::EPL];
   float* wout = weights != nullptr ? weights + ((long)bh * m + j) * g : nullptr;
   pool_group<DT, D, MODE>(krow, vrow, qrow, g, G, scale_log2, acck, accv, wout);
@@ -79,36 +88,43 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q_,
 
 template <int DT, int D, int MODE>
 void launch_pool_t(const void* q, const void* k, const void* v, void* ck, void* cv, int m_cap,
-                   float* weights, const Shape& sh, hipStream_t s) {
-  const long groups = (long)sh.B * sh.Hkv * sh.m();
+                   float* weights, const Shape& sh, const RowRange& rr, hipStream_t s) {
+  // group slots per (b, kv head): every group of a full prefill; at most
+  // Lq / g + 1 group ends fall among Lq consecutive rows of a chunk
+  const int gpb = rr.q_start == nullptr ? rr.Lq / sh.g : rr.Lq / sh.g + 1;
+  const long slots = (long)sh.B * sh.Hkv * gpb;
   const int waves = 4;
-  const long blocks = (groups + waves - 1) / waves;
+  const long blocks = (slots + waves - 1) / waves;
+  if (blocks == 0) return;
   const float scale_log2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((pool_kernel<DT, D, MODE>), dim3((unsigned)blocks), dim3(64 * waves), 0, s, q, k,
-                     v, ck, cv, weights, m_cap, sh.B, sh.Hq, sh.Hkv, sh.L, sh.g, scale_log2);
+                     v, ck, cv, weights, m_cap, rr.q_start, rr.q_len, gpb, sh.B, sh.Hq, sh.Hkv,
+                     rr.Lq, rr.Lk, sh.g, scale_log2);
 }
 
 template <int DT, int D>
 void launch_pool_mode(int mode, const void* q, const void* k, const void* v, void* ck, void* cv,
-                      int m_cap, float* weights, const Shape& sh, hipStream_t s) {
+                      int m_cap, float* weights, const Shape& sh, const RowRange& rr,
+                      hipStream_t s) {
   switch (mode) {
-    case kPoolSoftmaxHeads: launch_pool_t<DT, D, kPoolSoftmaxHeads>(q, k, v, ck, cv, m_cap, weights, sh, s); break;
-    case kPoolMean: launch_pool_t<DT, D, kPoolMean>(q, k, v, ck, cv, m_cap, weights, sh, s); break;
-    case kPoolMax: launch_pool_t<DT, D, kPoolMax>(q, k, v, ck, cv, m_cap, weights, sh, s); break;
-    default: launch_pool_t<DT, D, kPoolSoftmax>(q, k, v, ck, cv, m_cap, weights, sh, s); break;
+    case kPoolSoftmaxHeads: launch_pool_t<DT, D, kPoolSoftmaxHeads>(q, k, v, ck, cv, m_cap, weights, sh, rr, s); break;
+    case kPoolMean: launch_pool_t<DT, D, kPoolMean>(q, k, v, ck, cv, m_cap, weights, sh, rr, s); break;
+    case kPoolMax: launch_pool_t<DT, D, kPoolMax>(q, k, v, ck, cv, m_cap, weights, sh, rr, s); break;
+    default: launch_pool_t<DT, D, kPoolSoftmax>(q, k, v, ck, cv, m_cap, weights, sh, rr, s); break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_pool(const void* q, const void* k, const void* v, void* ck, void* cv, int m_cap,
-                       float* weights, const Shape& sh, int dt, int mode, hipStream_t s) {
+                       float* weights, const Shape& sh, const RowRange& rr, int dt, int mode,
+                       hipStream_t s) {
   if (dt == 0) {
-    if (sh.d == 64) launch_pool_mode<0, 64>(mode, q, k, v, ck, cv, m_cap, weights, sh, s);
-    else launch_pool_mode<0, 128>(mode, q, k, v, ck, cv, m_cap, weights, sh, s);
+    if (sh.d == 64) launch_pool_mode<0, 64>(mode, q, k, v, ck, cv, m_cap, weights, sh, rr, s);
+    else launch_pool_mode<0, 128>(mode, q, k, v, ck, cv, m_cap, weights, sh, rr, s);
   } else {
-    if (sh.d == 64) launch_pool_mode<1, 64>(mode, q, k, v, ck, cv, m_cap, weights, sh, s);
-    else launch_pool_mode<1, 128>(mode, q, k, v, ck, cv, m_cap, weights, sh, s);
+    if (sh.d == 64) launch_pool_mode<1, 64>(mode, q, k, v, ck, cv, m_cap, weights, sh, rr, s);
+    else launch_pool_mode<1, 128>(mode, q, k, v, ck, cv, m_cap, weights, sh, rr, s);
   }
   return hipGetLastError();
 }

@@ -52,7 +52,9 @@ struct PrefillParams {
   const uint16_t* ck;
   const uint16_t* cv;
   void* out;
-  int B, Hq, Hkv, L, g, w, m_cap;
+  const int32_t* q_start;  // per-sequence query rows (RowRange); null: every row
+  const int32_t* q_len;
+  int B, Hq, Hkv, Lq, Lk, g, w, m_cap;
   int G, Hw, RP;        // heads per workgroup, rows per head per workgroup
   int nPB, nHG, U;      // position blocks, head groups per kv head, units
   int xcd;              // 1 when units split evenly over 8 XCDs
@@ -158,23 +160,38 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int hg = u % P.nHG;
   const int b = kvp / P.Hkv;
   const int kvh = kvp % P.Hkv;
-  const int L = P.L, g = P.g, w = P.w;
+  const int g = P.g, w = P.w;
   const int h = kvh * P.G + hg * P.Hw + (wave % P.Hw);
-  const int P_lo = pb * P.RP;
-  const int P_hi = min(L - 1, P_lo + P.RP - 1);
-  const int p0 = P_lo + 32 * (wave / P.Hw);
+  const int row0 = pb * P.RP + 32 * (wave / P.Hw);  // local row of the wave's first row
+  // sequence b's rows: positions qs .. qs + ql - 1 at local rows 0 .. ql - 1
+  const SeqRows sr = seq_rows(P.q_start, P.q_len, b, P.Lq, P.Lk, g, w, P.m_cap);
+  if (!sr.ok) {  // rows that do not fit the buffers: NaN, nothing read
+    if (row0 + j < P.Lq) {
+      const long orow = (((long)b * P.Hq + h) * P.Lq + row0 + j) * D;
+      for (int e = hh; e < D; e += 2) {
+        if (OT == 1) static_cast<uint16_t*>(P.out)[orow + e] = 0x7fc0;
+        else static_cast<float*>(P.out)[orow + e] = NAN;
+      }
+    }
+    return;
+  }
+  const int qs = sr.qs, Le = sr.qs + sr.ql;  // first position, one past the last
+  if (pb * P.RP >= sr.ql) return;             // the whole workgroup lies past the end
+  const int P_lo = qs + pb * P.RP;
+  const int P_hi = min(Le - 1, P_lo + P.RP - 1);
+  const int p0 = qs + row0;
 
   // ---- this lane's query row and the wave's row range
   const int t_raw = p0 + j;
-  const int t = min(t_raw, L - 1);
+  const int t = min(t_raw, Le - 1);
   const int my_nc = n_core(t, g, w);
   const int my_lo = win_lo(t, w);
   // Per-wave and per-workgroup bounds are uniform; readfirstlane keeps them in
   // scalar registers (the integer divisions inside n_core run on the vector
   // ALUs), so that the tile branches below stay scalar branches.
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
-  const int w_lo = uni(min(p0, L - 1));
-  const int w_hi = uni(min(p0 + 31, L - 1));
+  const int w_lo = uni(min(p0, Le - 1));
+  const int w_hi = uni(min(p0 + 31, Le - 1));
   const int wnc_lo = uni(n_core(w_lo, g, w)), wnc_hi = uni(n_core(w_hi, g, w));
   const int wlo_lo = uni(win_lo(w_lo, w)), wlo_hi = uni(win_lo(w_hi, w));
 
@@ -187,15 +204,15 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int n_tiles = uni(n_ct + n_rt);
 
   const long kvrow = (long)kvp;
-  const uint16_t* kbase = P.k + kvrow * L * D;
-  const uint16_t* vbase = P.v + kvrow * L * D;
+  const uint16_t* kbase = P.k + kvrow * P.Lk * D;
+  const uint16_t* vbase = P.v + kvrow * P.Lk * D;
   const uint16_t* ckbase = P.ck + kvrow * P.m_cap * D;
   const uint16_t* cvbase = P.cv + kvrow * P.m_cap * D;
 
   // ---- Q fragment: B operand, lane holds Q[row j][16ks + 8hh .. +7]
   bf16x8 qf[KS];
   {
-    const uint16_t* qrow = P.q + (((long)b * P.Hq + h) * L + t) * D;
+    const uint16_t* qrow = P.q + (((long)b * P.Hq + h) * P.Lq + (t - qs)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hh);
     // Use the fragments here, so that the compiler waits for these loads now:
@@ -448,8 +465,8 @@ void prefill_mfma_kernel(PrefillParams P) {
   // ---- normalise and store: lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
   const float ltot = pair_sum(l);
   const float inv = 1.0f / ltot;
-  if (t_raw < L) {
-    const long orow = (((long)b * P.Hq + h) * L + t_raw) * D;
+  if (t_raw < Le) {
+    const long orow = (((long)b * P.Hq + h) * P.Lq + (t_raw - qs)) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -483,7 +500,7 @@ int gcd_int(int a, int b) {
 
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* ck,
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
-                               hipStream_t s) {
+                               const RowRange& rr, hipStream_t s) {
   PrefillParams P;
   P.q = static_cast<const uint16_t*>(q);
   P.k = static_cast<const uint16_t*>(k);
@@ -494,14 +511,17 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
   P.B = sh.B;
   P.Hq = sh.Hq;
   P.Hkv = sh.Hkv;
-  P.L = sh.L;
+  P.q_start = rr.q_start;
+  P.q_len = rr.q_len;
+  P.Lq = rr.Lq;
+  P.Lk = rr.Lk;
   P.g = sh.g;
   P.w = sh.w;
   P.m_cap = m_cap;
   P.G = sh.G();
   P.Hw = gcd_int(P.G, kWaves);
   P.RP = 32 * (kWaves / P.Hw);
-  P.nPB = (sh.L + P.RP - 1) / P.RP;
+  P.nPB = (rr.Lq + P.RP - 1) / P.RP;
   P.nHG = P.G / P.Hw;
   P.U = sh.B * sh.Hkv * P.nHG;
   P.xcd = (P.U % 8 == 0) ? 1 : 0;

@@ -24,7 +24,8 @@ template <int DT, int OT, int D>
 __global__ __launch_bounds__(256) void prefill_valu_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const void* __restrict__ ck_, const void* __restrict__ cv_, void* __restrict__ out_, int m_cap,
-    int Hq, int Hkv, int L, int g, int w, float scale_log2) {
+    const int32_t* __restrict__ q_start, const int32_t* __restrict__ q_len, int Hq, int Hkv, int Lq,
+    int Lk, int g, int w, float scale_log2) {
   typedef Elem<DT> E;
   typedef typename E::T T;
   constexpr int DH = D / 2;
@@ -38,9 +39,23 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
   const int b = blockIdx.z;
   const int G = Hq / Hkv;
   const int hk = h / G;
-  const int t0 = blockIdx.x * kRows;
-  const int t_hi = min(L - 1, t0 + kRows - 1);
-  const int t = min(t0 + r, L - 1);  // rows past L compute a duplicate and store nothing
+  // sequence b's rows: positions qs .. qs + ql - 1 at local rows 0 .. ql - 1
+  const SeqRows sr = seq_rows(q_start, q_len, b, Lq, Lk, g, w, m_cap);
+  const int r0 = blockIdx.x * kRows;  // local row of the block's first row
+  typedef Elem<OT> EO;
+  typename EO::T* out = static_cast<typename EO::T*>(out_);
+  if (!sr.ok) {  // rows that do not fit the buffers: NaN, nothing read
+    if (r0 + r < Lq) {
+      const long orow = ((long)(b * Hq + h) * Lq + r0 + r) * D + half * DH;
+      for (int e = 0; e < DH; ++e) EO::store(out, orow + e, NAN);
+    }
+    return;
+  }
+  if (r0 >= sr.ql) return;
+  const int qs = sr.qs, Le = sr.qs + sr.ql;
+  const int t0 = qs + r0;
+  const int t_hi = min(Le - 1, t0 + kRows - 1);
+  const int t = min(t0 + r, Le - 1);  // rows past the end compute a duplicate and store nothing
 
   const T* q = static_cast<const T*>(q_);
   const T* kk = static_cast<const T*>(k_);
@@ -49,7 +64,7 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
   const T* cv = static_cast<const T*>(cv_);
 
   float qr[DH], acc[DH];
-  const long qrow = ((long)(b * Hq + h) * L + t) * D + half * DH;
+  const long qrow = ((long)(b * Hq + h) * Lq + (t - qs)) * D + half * DH;
 #pragma unroll
   for (int e = 0; e < DH; ++e) {
     qr[e] = E::load(q, qrow + e);
@@ -78,7 +93,7 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
         kx = E::load(ck, off);
         vx = E::load(cv, off);
       } else if (f < total) {
-        const long off = (kv_base * L + raw_lo + (f - nc_hi)) * D + e;
+        const long off = (kv_base * Lk + raw_lo + (f - nc_hi)) * D + e;
         kx = E::load(kk, off);
         vx = E::load(vv, off);
       }
@@ -120,11 +135,9 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
     }
     mrun = mnew;
   }
-  if (t0 + r < L) {
-    typedef Elem<OT> EO;
-    typename EO::T* out = static_cast<typename EO::T*>(out_);
+  if (t0 + r < Le) {
     const float inv = 1.0f / lrun;
-    const long orow = ((long)(b * Hq + h) * L + t) * D + half * DH;
+    const long orow = ((long)(b * Hq + h) * Lq + (t - qs)) * D + half * DH;
 #pragma unroll
     for (int e = 0; e < DH; ++e) EO::store(out, orow + e, acc[e] * inv);
   }
@@ -132,27 +145,28 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
 
 template <int DT, int OT, int D>
 void launch_t(const void* q, const void* k, const void* v, const void* ck, const void* cv,
-              int m_cap, void* out, const Shape& sh, hipStream_t s) {
-  dim3 grid((sh.L + kRows - 1) / kRows, sh.Hq, sh.B);
+              int m_cap, void* out, const Shape& sh, const RowRange& rr, hipStream_t s) {
+  dim3 grid((rr.Lq + kRows - 1) / kRows, sh.Hq, sh.B);
   const float scale_log2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((prefill_valu_kernel<DT, OT, D>), grid, dim3(256), 0, s, q, k, v, ck, cv, out,
-                     m_cap, sh.Hq, sh.Hkv, sh.L, sh.g, sh.w, scale_log2);
+                     m_cap, rr.q_start, rr.q_len, sh.Hq, sh.Hkv, rr.Lq, rr.Lk, sh.g, sh.w,
+                     scale_log2);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, const void* ck,
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
-                               int dt, hipStream_t s) {
+                               const RowRange& rr, int dt, hipStream_t s) {
   if (dt == 0) {
-    if (sh.d == 64) launch_t<0, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, s);
-    else launch_t<0, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, s);
+    if (sh.d == 64) launch_t<0, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
+    else launch_t<0, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
   } else if (out_dt == 1) {
-    if (sh.d == 64) launch_t<1, 1, 64>(q, k, v, ck, cv, m_cap, out, sh, s);
-    else launch_t<1, 1, 128>(q, k, v, ck, cv, m_cap, out, sh, s);
+    if (sh.d == 64) launch_t<1, 1, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
+    else launch_t<1, 1, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
   } else {
-    if (sh.d == 64) launch_t<1, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, s);
-    else launch_t<1, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, s);
+    if (sh.d == 64) launch_t<1, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
+    else launch_t<1, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
   }
   return hipGetLastError();
 }

@@ -138,6 +138,50 @@ def test_decode_mode_validation(cca_lib, mode, kw, code):
     assert decode_ex(cca_lib, mode, **kw) == code
 
 
+def pool_chunk(lib, q=FAKE, k=FAKE, v=FAKE, ck=FAKE, cv=FAKE, m_cap=64, qs=FAKE, ql=FAKE, B=2, Hq=4,
+               Hkv=2, Lq=256, Lk=1024, d=128, g=16, dt=1, mode=0):
+    return lib.cca_pool_core_chunk(P(q), P(k), P(v), P(ck), P(cv), m_cap, P(qs), P(ql), B, Hq, Hkv, Lq,
+                                   Lk, d, g, dt, mode, None)
+
+
+def prefill_chunk(lib, q=FAKE, k=FAKE, v=FAKE, ck=FAKE, cv=FAKE, m_cap=64, out=FAKE, out_dt=1, qs=FAKE,
+                  ql=FAKE, B=2, Hq=4, Hkv=2, Lq=256, Lk=1024, d=128, g=16, w=64, dt=1):
+    return lib.cca_attn_prefill_chunk(P(q), P(k), P(v), P(ck), P(cv), m_cap, P(out), out_dt, P(qs), P(ql),
+                                      B, Hq, Hkv, Lq, Lk, d, g, w, dt, None)
+
+
+def fill_ring(lib, k=FAKE, v=FAKE, rk=FAKE, rv=FAKE, R=1024, sl=FAKE, B=2, Hkv=2, Lk=4096, d=128, dt=1):
+    return lib.cca_cache_fill_ring(P(k), P(v), P(rk), P(rv), R, P(sl), B, Hkv, Lk, d, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=None), INV), (dict(ql=FAKE + 2), INV), (dict(Lq=0), INV), (dict(Lk=0), INV), (dict(g=0), INV),
+    (dict(mode=7), INV), (dict(q=None), INV), (dict(k=None), INV), (dict(m_cap=-1), INV),
+    (dict(ck=None), INV), (dict(d=96), UNS), (dict(mode=1, Hq=18, Hkv=2), UNS),
+    (dict(m_cap=0, ck=None, cv=None), OK),  # no core slot: nothing to do
+    (dict(q=None, mode=_lib.CCA_POOL_MAX, m_cap=0), OK),
+])
+def test_pool_chunk_validation(cca_lib, kw, code):
+    assert pool_chunk(cca_lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qs=None), INV), (dict(ql=None), INV), (dict(qs=FAKE + 1), INV), (dict(Lq=0), INV), (dict(w=0), INV),
+    (dict(out=None), INV), (dict(m_cap=-1), INV), (dict(cv=None), INV), (dict(dt=0, out_dt=1), UNS),
+    (dict(Hkv=3), UNS), (dict(out_dt=4), INV),
+])
+def test_prefill_chunk_validation(cca_lib, kw, code):
+    assert prefill_chunk(cca_lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(R=0), INV), (dict(Lk=0), INV), (dict(sl=None), INV), (dict(sl=FAKE + 2), INV), (dict(rk=None), INV),
+    (dict(d=32), UNS), (dict(B=1 << 9, Hkv=1 << 8), UNS),
+])
+def test_fill_ring_validation(cca_lib, kw, code):
+    assert fill_ring(cca_lib, **kw) == code
+
+
 def test_decode_workspace_size(cca_lib):
     f = cca_lib.cca_decode_workspace_bytes
     n = f(8, 32, 8, 128, 4112, 16, 1024)
