@@ -1,0 +1,187 @@
+"""fp64 CPU oracle of the CCA attention backward pass (gradients of the forward
+in ``cca_oracle``).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing in the product
+path imports this module.
+
+The pages fine-tune pretrained models with CCA attention in place (paper
+card, summary and key results: full and partial fine-tuning; rebuttal, answer
+on the fine-tuning setting), which needs the gradients of the two steps of the
+forward; they print none.  The oracle takes them from the
+chain rule, step by step, in the forward's order reversed:
+
+1. Fusion ([digest], Method, fusion formula).  Row t has scores
+   S_k = q_t . key_k / sqrt(d) over its visible keys (cores CK_0..CK_{n-1},
+   then raw K_lo..K_t), P = softmax(S) and o_t = sum_k P_k value_k.  With an
+   upstream gradient dO_t:
+       dP_k     = dO_t . value_k
+       dS_k     = P_k (dP_k - sum_k' P_k' dP_k')            (softmax Jacobian)
+       dq_t     = sum_k dS_k key_k / sqrt(d)
+       dkey_k  += dS_k q_t / sqrt(d),   dvalue_k += P_k dO_t
+   summed over every row (and query head) that sees key k; a core's
+   gradient goes to dCK / dCV.
+
+2. Global-aware pooling ([digest], Method, pooling formula; modes of reading
+   R-13).  For group j with weights a (over its g tokens), CK_j = sum a K and
+   CV_j = sum a V:
+       dK[tau] += a_tau dCK_j,   dV[tau] += a_tau dCV_j
+       da_tau   = dCK_j . K[tau] + dCV_j . V[tau]
+   and for the softmax rules, a = softmax(s) with s_tau = q . K[tau] / sqrt(d):
+       ds_tau   = a_tau (da_tau - sum a da)
+       dK[tau] += ds_tau q / sqrt(d),   dq = sum_tau ds_tau K[tau] / sqrt(d),
+   where q is the mean of the G heads' last-token queries (rule "softmax":
+   each head's query row gets dq / G) or each head's own query with its own
+   softmax, averaged over the heads (rule "softmax_heads": the head's a is
+   that head's softmax, and its da is divided by G).  Rule "mean" has fixed
+   weights 1/g; rule "max" routes each component's gradient to the token that
+   holds the maximum (the first one on ties, a reading: R-15).
+
+Each function below computes its row or group on its own, with numpy
+products and sums as the only library primitives.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .cca_oracle import _f64, _softmax, group_last, n_core, pool_core, win_lo, attn_prefill
+
+
+def _scale(d: int) -> float:
+    """Score scale of both softmaxes, 1/sqrt(d) (reading R-4)."""
+    return 1.0 / math.sqrt(d)
+
+
+def _softmax_backward(p, dp):
+    """Gradient through p = softmax(s) along the last axis: p * (dp - sum p dp)."""
+    return p * (dp - np.sum(p * dp, axis=-1, keepdims=True))
+
+
+def attn_backward(Q, K, V, CK, CV, g: int, w: int, dO):
+    """Gradients of the fused prefill (step 1) for upstream dO [B,Hq,L,d].
+
+    Returns dQ [B,Hq,L,d], dK, dV [B,Hkv,L,d] (raw keys/values) and dCK, dCV
+    [B,Hkv,m,d] (cores), all fp64; m = CK.shape[2].
+    """
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    Q, K, V, CK, CV, dO = (_f64(x) for x in (Q, K, V, CK, CV, dO))
+    scale = _scale(d)
+    dQ = np.zeros_like(Q)
+    dK, dV = np.zeros_like(K), np.zeros_like(V)
+    dCK, dCV = np.zeros_like(CK), np.zeros_like(CV)
+    for t in range(L):
+        nc, lo = n_core(t, g, w), win_lo(t, w)
+        for h in range(Hq):
+            hk = h // G
+            for b in range(B):
+                keys = np.concatenate([CK[b, hk, :nc], K[b, hk, lo : t + 1]], axis=0)
+                vals = np.concatenate([CV[b, hk, :nc], V[b, hk, lo : t + 1]], axis=0)
+                q = Q[b, h, t]
+                p = _softmax(keys @ q * scale)
+                dp = vals @ dO[b, h, t]
+                ds = _softmax_backward(p, dp)
+                dQ[b, h, t] = ds @ keys * scale
+                dkeys = np.outer(ds, q) * scale
+                dvals = np.outer(p, dO[b, h, t])
+                dCK[b, hk, :nc] += dkeys[:nc]
+                dCV[b, hk, :nc] += dvals[:nc]
+                dK[b, hk, lo : t + 1] += dkeys[nc:]
+                dV[b, hk, lo : t + 1] += dvals[nc:]
+    return dQ, dK, dV, dCK, dCV
+
+
+def pool_backward(Q, K, V, g: int, dCK, dCV, mode: str = "softmax"):
+    """Gradients of pooling (step 2) for upstream dCK, dCV [B,Hkv,m,d].
+
+    Returns dQ [B,Hq,L,d] (non-zero only at group-end rows of the softmax
+    rules), dK, dV [B,Hkv,L,d]; fp64.
+    """
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    m = dCK.shape[2]
+    Q, K, V, dCK, dCV = (_f64(x) for x in (Q, K, V, dCK, dCV))
+    scale = _scale(d)
+    dQ = np.zeros_like(Q)
+    dK, dV = np.zeros_like(K), np.zeros_like(V)
+    for b in range(B):
+        for hk in range(Hkv):
+            heads = range(hk * G, hk * G + G)
+            for j in range(m):
+                rows = slice(j * g, j * g + g)
+                Kg, Vg = K[b, hk, rows], V[b, hk, rows]
+                dck, dcv = dCK[b, hk, j], dCV[b, hk, j]
+                last = group_last(j, g)
+                if mode == "max":
+                    # R-15: each component's gradient goes to the first token holding the maximum
+                    for e in range(d):
+                        dK[b, hk, j * g + int(np.argmax(Kg[:, e])), e] += dck[e]
+                        dV[b, hk, j * g + int(np.argmax(Vg[:, e])), e] += dcv[e]
+                    continue
+                if mode == "mean":
+                    dK[b, hk, rows] += dck / g
+                    dV[b, hk, rows] += dcv / g
+                    continue
+                da = Kg @ dck + Vg @ dcv                                      # [g]
+                if mode == "softmax":
+                    qbar = np.mean([Q[b, h, last] for h in heads], axis=0)
+                    a = _softmax(Kg @ qbar * scale)
+                    ds = _softmax_backward(a, da)
+                    dK[b, hk, rows] += np.outer(a, dck) + np.outer(ds, qbar) * scale
+                    dV[b, hk, rows] += np.outer(a, dcv)
+                    dq = ds @ Kg * scale
+                    for h in heads:
+                        dQ[b, h, last] += dq / G
+                elif mode == "softmax_heads":
+                    a_sum = np.zeros(g)
+                    for h in heads:
+                        ah = _softmax(Kg @ Q[b, h, last] * scale)
+                        a_sum += ah / G
+                        dsh = _softmax_backward(ah, da) / G
+                        dK[b, hk, rows] += np.outer(dsh, Q[b, h, last]) * scale
+                        dQ[b, h, last] += dsh @ Kg * scale
+                    dK[b, hk, rows] += np.outer(a_sum, dck)
+                    dV[b, hk, rows] += np.outer(a_sum, dcv)
+                else:
+                    raise ValueError(f"unknown pooling mode {mode!r}")
+    return dQ, dK, dV
+
+
+def backward(Q, K, V, g: int, w: int, dO, mode: str = "softmax"):
+    """Gradients of the whole forward (pooling, then fused prefill) w.r.t. Q,
+    K and V, for upstream dO: step 1, then step 2 on step 1's core gradients.
+    Returns dQ [B,Hq,L,d], dK, dV [B,Hkv,L,d] in fp64."""
+    CK, CV, _ = pool_core(Q, K, V, g, mode)
+    dQ, dK, dV, dCK, dCV = attn_backward(Q, K, V, CK, CV, g, w, dO)
+    pQ, pK, pV = pool_backward(Q, K, V, g, dCK, dCV, mode)
+    return dQ + pQ, dK + pK, dV + pV
+
+
+def loss(Q, K, V, g: int, w: int, dO, mode: str = "softmax") -> float:
+    """The scalar whose gradient ``backward`` returns: sum(O * dO)."""
+    CK, CV, _ = pool_core(Q, K, V, g, mode)
+    return float(np.sum(attn_prefill(Q, K, V, CK, CV, g, w) * _f64(dO)))
+
+
+def row_lse(Q, K, CK, g: int, w: int):
+    """Natural-log log-sum-exp of each row's scores, [B,Hq,L] (the statistic a
+    forward pass hands to the backward)."""
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    Q, K, CK = _f64(Q), _f64(K), _f64(CK)
+    out = np.empty((B, Hq, L))
+    for t in range(L):
+        nc, lo = n_core(t, g, w), win_lo(t, w)
+        for h in range(Hq):
+            keys = np.concatenate([CK[:, h // G, :nc], K[:, h // G, lo : t + 1]], axis=1)
+            s = np.einsum("bkd,bd->bk", keys, Q[:, h, t]) / math.sqrt(d)
+            mx = s.max(axis=1)
+            out[:, h, t] = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+    return out
+
+
+__all__ = ["attn_backward", "pool_backward", "backward", "loss", "row_lse"]
