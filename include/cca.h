@@ -157,6 +157,51 @@ cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, cons
                                int kernel, void* stream);
 
 /*
+ * Training: the forward with its softmax statistic, and the backward pass.
+ * The pages fine-tune pretrained models with CCA attention in place (paper
+ * card, summary and key results; rebuttal, answer on the fine-tuning
+ * setting); the gradients follow from the chain rule through the fusion and
+ * pooling formulas (digest, "Method").
+ *
+ * cca_attn_prefill_train - cca_attn_prefill (automatic kernel) that also
+ *   writes lse: fp32 [B,Hq,L], each row's natural-log log-sum-exp of its
+ *   scores q_t . key / sqrt(d) over its visible keys.
+ */
+cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, const void* core_k,
+                                  const void* core_v, int m_cap, void* out, cca_dtype out_dt,
+                                  float* lse, int B, int Hq, int Hkv, int L, int d, int g, int w,
+                                  cca_dtype dt, void* stream);
+
+/*
+ * cca_attn_backward_workspace_bytes - device workspace cca_attn_backward needs
+ *   (fp32 row statistics [B,Hq,L] and core gradients 2 x [B,Hkv,L/g,d]).
+ */
+size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g);
+
+/*
+ * cca_attn_backward - gradients of the whole forward (pooling with rule
+ *   pool_mode, then the fused prefill) w.r.t. q, k and v, given the upstream
+ *   gradient dout of out:
+ *     q, k, v, core_k, core_v, out, dout in dt (out and dout [B,Hq,L,d]; out
+ *     and the cores as the forward wrote them); lse fp32 [B,Hq,L] from
+ *     cca_attn_prefill_train; dq [B,Hq,L,d], dk, dv [B,Hkv,L,d] fp32, fully
+ *     overwritten.  Per row: dS = P (dP - dout . out); dq, and the raw and
+ *     core key/value gradients, as in the chain rule; the core gradients then
+ *     flow through pooling into the group's k, v and the pooling query rows.
+ *     Max pooling routes each component's gradient to the first token holding
+ *     the maximum.  workspace: device memory of at least
+ *     cca_attn_backward_workspace_bytes bytes; no initialisation needed.
+ * Errors: INVALID_ARG (null/misaligned pointers, sizes, unknown mode),
+ *   UNSUPPORTED (d, dt, Hq % Hkv, per-head pooling with G > 8, B*Hkv or Hq >
+ *   65535), CAPACITY (m_cap < L/g, workspace too small).
+ */
+cca_status cca_attn_backward(const void* q, const void* k, const void* v, const void* core_k,
+                             const void* core_v, int m_cap, const void* out, const float* lse,
+                             const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                             size_t workspace_bytes, int B, int Hq, int Hkv, int L, int d, int g,
+                             int w, cca_dtype dt, int pool_mode, void* stream);
+
+/*
  * Chunked and variable-length prefill.  The article notes that CCA generates
  * with token counts that are not multiples of g; a long prompt is processed in
  * chunks, and sequences of one batch have their own lengths.  Each sequence b

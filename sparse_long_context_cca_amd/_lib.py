@@ -22,7 +22,8 @@ CCA_POOL_SOFTMAX, CCA_POOL_SOFTMAX_HEADS, CCA_POOL_MEAN, CCA_POOL_MAX = range(4)
 EXPORTS = ["cca_version", "cca_status_string", "cca_last_error", "cca_visibility_table",
            "cca_pool_core", "cca_pool_core_ex", "cca_attn_prefill", "cca_attn_prefill_ex",
            "cca_decode_workspace_bytes", "cca_attn_decode", "cca_attn_decode_ex",
-           "cca_pool_core_chunk", "cca_attn_prefill_chunk", "cca_cache_fill_ring"]
+           "cca_pool_core_chunk", "cca_attn_prefill_chunk", "cca_cache_fill_ring",
+           "cca_attn_prefill_train", "cca_attn_backward_workspace_bytes", "cca_attn_backward"]
 
 
 class CCAError(RuntimeError):
@@ -59,6 +60,9 @@ def load() -> ctypes.CDLL:
         "cca_pool_core_chunk": ([P, P, P, P, P, I, P, P, I, I, I, I, I, I, I, I, I, P], I),
         "cca_attn_prefill_chunk": ([P, P, P, P, P, I, P, I, P, P, I, I, I, I, I, I, I, I, I, P], I),
         "cca_cache_fill_ring": ([P, P, P, P, I, P, I, I, I, I, I, P], I),
+        "cca_attn_prefill_train": ([P, P, P, P, P, I, P, I, P, I, I, I, I, I, I, I, I, P], I),
+        "cca_attn_backward_workspace_bytes": ([I, I, I, I, I, I], S),
+        "cca_attn_backward": ([P, P, P, P, P, I, P, P, P, P, P, P, P, S, I, I, I, I, I, I, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -193,3 +197,35 @@ def cca_cache_fill_ring(k, v, ring_k, ring_v, seq_len, stream=None) -> None:
     R = ring_k.shape[2]
     _check(load().cca_cache_fill_ring(_ptr(k), _ptr(v), _ptr(ring_k), _ptr(ring_v), R, _rows(seq_len),
                                       B, Hkv, Lk, d, _dt(k), _stream(stream)))
+
+
+def cca_attn_prefill_train(q, k, v, core_k, core_v, out, lse, g: int, w: int, stream=None) -> None:
+    """cca_attn_prefill that also writes lse fp32 [B,Hq,L], each row's log-sum-exp of its scores."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    m_cap = core_k.shape[2] if core_k is not None else 0
+    if lse.dtype != torch.float32:
+        raise CCAError(CCA_ERR_INVALID_ARG, "lse must be fp32")
+    _check(load().cca_attn_prefill_train(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
+                                         _ptr(out), _dt(out), _ptr(lse), B, Hq, Hkv, L, d, g, w, _dt(q),
+                                         _stream(stream)))
+
+
+def cca_attn_backward_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, d: int, g: int) -> int:
+    return int(load().cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g))
+
+
+def cca_attn_backward(q, k, v, core_k, core_v, out, lse, dout, dq, dk, dv, workspace, g: int, w: int,
+                      pool_mode: int = CCA_POOL_SOFTMAX, stream=None) -> None:
+    """Gradients dq [B,Hq,L,d], dk, dv [B,Hkv,L,d] (fp32, overwritten) of the forward (pooling with
+    rule pool_mode, then the fused prefill) for the upstream gradient dout of out."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    m_cap = core_k.shape[2] if core_k is not None else 0
+    for t in (dq, dk, dv):
+        if t.dtype != torch.float32:
+            raise CCAError(CCA_ERR_INVALID_ARG, "gradients are fp32")
+    _check(load().cca_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap, _ptr(out),
+                                    _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), B, Hq, Hkv, L, d, g, w,
+                                    _dt(q), pool_mode, _stream(stream)))

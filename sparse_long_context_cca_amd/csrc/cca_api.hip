@@ -242,10 +242,94 @@ cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, cons
   rr.Lq = rr.Lk = L;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (kernel == 2)
-    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, s),
+    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, nullptr, s),
                     fn);
   return from_hip(
-      cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, dt, s), fn);
+      cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, nullptr, dt, s), fn);
+}
+
+cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, const void* core_k,
+                                  const void* core_v, int m_cap, void* out, cca_dtype out_dt,
+                                  float* lse, int B, int Hq, int Hkv, int L, int d, int g, int w,
+                                  cca_dtype dt, void* stream) {
+  const char* fn = "cca_attn_prefill_train";
+  if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return fail(CCA_ERR_INVALID_ARG, "%s: lse is NULL or not 4-byte aligned", fn);
+  if (L < 1 || g < 1 || w < 1)
+    return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
+  cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_out_dt(fn, out_dt, dt);
+  if (st != CCA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  const int m = L / g;
+  if (m_cap < m) return fail(CCA_ERR_CAPACITY, "%s: m_cap=%d < L/g=%d", fn, m_cap, m);
+  if (cca::n_core(L - 1, g, w) > 0) {
+    REQUIRE_PTR(core_k);
+    REQUIRE_PTR(core_v);
+  }
+  st = check_sizes(fn, (long long)B * Hq * L * d, (long long)B * Hkv * L * d,
+                   (long long)B * Hkv * m_cap * d);
+  if (st != CCA_OK) return st;
+  cca::Shape sh{B, Hq, Hkv, L, d, g, w};
+  cca::RowRange rr;
+  rr.Lq = rr.Lk = L;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dt == CCA_BF16)
+    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, lse, s),
+                    fn);
+  return from_hip(
+      cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, lse, dt, s), fn);
+}
+
+size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || d < 1 || g < 1) return 0;
+  return cca::backward_workspace_bytes(B, Hq, Hkv, L, d, g);
+}
+
+cca_status cca_attn_backward(const void* q, const void* k, const void* v, const void* core_k,
+                             const void* core_v, int m_cap, const void* out, const float* lse,
+                             const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                             size_t workspace_bytes, int B, int Hq, int Hkv, int L, int d, int g,
+                             int w, cca_dtype dt, int pool_mode, void* stream) {
+  const char* fn = "cca_attn_backward";
+  if (L < 1 || g < 1 || w < 1)
+    return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
+  cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_pool_mode(fn, pool_mode, Hq, Hkv);
+  if (st != CCA_OK) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(dout);
+  REQUIRE_PTR(dq);
+  REQUIRE_PTR(dk);
+  REQUIRE_PTR(dv);
+  const int m = L / g;
+  if (m_cap < m) return fail(CCA_ERR_CAPACITY, "%s: m_cap=%d < L/g=%d", fn, m_cap, m);
+  if (m > 0) {
+    REQUIRE_PTR(core_k);
+    REQUIRE_PTR(core_v);
+  }
+  st = check_sizes(fn, (long long)B * Hq * L * d, (long long)B * Hkv * L * d,
+                   (long long)B * Hkv * m_cap * d);
+  if (st != CCA_OK) return st;
+  if ((long long)B * Hkv > 65535 || (long long)Hq > 65535)
+    return fail(CCA_ERR_UNSUPPORTED, "%s: B*Hkv or Hq exceeds 65535", fn);
+  const size_t need = cca::backward_workspace_bytes(B, Hq, Hkv, L, d, g);
+  if (workspace_bytes < need)
+    return fail(CCA_ERR_CAPACITY, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
+  REQUIRE_PTR(workspace);
+  cca::Shape sh{B, Hq, Hkv, L, d, g, w};
+  return from_hip(cca::launch_backward(q, k, v, core_k, core_v, m_cap, out, lse, dout, dq, dk, dv,
+                                       workspace, sh, dt, pool_mode, static_cast<hipStream_t>(stream)),
+                  fn);
 }
 
 cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, const void* core_k,
@@ -281,10 +365,10 @@ cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, c
   rr.Lk = Lk;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dt == CCA_BF16)
-    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, s),
+    return from_hip(cca::launch_prefill_mfma(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, nullptr, s),
                     fn);
   return from_hip(
-      cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, dt, s), fn);
+      cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, nullptr, dt, s), fn);
 }
 
 cca_status cca_cache_fill_ring(const void* k, const void* v, void* ring_k, void* ring_v, int R,

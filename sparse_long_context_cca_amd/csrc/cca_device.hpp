@@ -97,5 +97,6 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 }  // namespace cca

@@ -38,14 +38,16 @@ hipError_t launch_pool(const void* q, const void* k, const void* v, void* ck, vo
                        hipStream_t s);
 
 // Vector-ALU prefill (fp32 math, any input dtype).
+// lse: null, or fp32 [B,Hq,Lq] receiving each row's natural-log log-sum-exp
+// of its scores (the statistic a backward pass needs).
 hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, const void* ck,
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
-                               const RowRange& rr, int dt, hipStream_t s);
+                               const RowRange& rr, float* lse, int dt, hipStream_t s);
 
 // bf16 matrix-core prefill.
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* ck,
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
-                               const RowRange& rr, hipStream_t s);
+                               const RowRange& rr, float* lse, hipStream_t s);
 
 struct DecodePlan {
   int splits;         // key-range splits per (b, kv head)
@@ -57,6 +59,14 @@ hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void
                          void* ring_v, int R, void* ck, void* cv, int m_cap, int32_t* pos,
                          int advance_pos, void* out, int out_dt, void* ws, const DecodePlan& plan,
                          const Shape& sh, int dt, int pool_mode, hipStream_t s);
+
+// Backward pass (cca_backward.hip).  Workspace: D [B,Hq,L] and the core
+// gradients dCK, dCV [B,Hkv,L/g,d], all fp32.
+size_t backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* ck,
+                           const void* cv, int m_cap, const void* out, const float* lse,
+                           const void* dout, float* dq, float* dk, float* dv, void* ws,
+                           const Shape& sh, int dt, int pool_mode, hipStream_t s);
 
 // Copies positions max(0, len-R) .. len-1 of sequence b's K and V (len =
 // seq_len[b], device) into ring slot p % R; a len outside 0 .. Lk copies nothing.

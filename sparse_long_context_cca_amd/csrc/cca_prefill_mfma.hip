@@ -52,6 +52,7 @@ struct PrefillParams {
   const uint16_t* ck;
   const uint16_t* cv;
   void* out;
+  float* lse;  // null, or the natural-log log-sum-exp of each row's scores [B,Hq,Lq]
   const int32_t* q_start;  // per-sequence query rows (RowRange); null: every row
   const int32_t* q_len;
   int B, Hq, Hkv, Lq, Lk, g, w, m_cap;
@@ -482,6 +483,10 @@ void prefill_mfma_kernel(PrefillParams P) {
           *reinterpret_cast<float4*>(out + orow + d0) = make_float4(x0, x1, x2, x3);
         }
       }
+    // the softmax's normaliser for a backward pass: probabilities are
+    // exp2(s c - m c) / ltot, so log-sum-exp (natural log) = (m c + log2 ltot) ln 2
+    if (P.lse != nullptr && hh == 0)
+      P.lse[((long)b * P.Hq + h) * P.Lq + (t_raw - qs)] = (m * c + log2f(ltot)) * kLn2;
   }
 }
 
@@ -500,7 +505,7 @@ int gcd_int(int a, int b) {
 
 hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, const void* ck,
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
-                               const RowRange& rr, hipStream_t s) {
+                               const RowRange& rr, float* lse, hipStream_t s) {
   PrefillParams P;
   P.q = static_cast<const uint16_t*>(q);
   P.k = static_cast<const uint16_t*>(k);
@@ -508,6 +513,7 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
   P.ck = static_cast<const uint16_t*>(ck);
   P.cv = static_cast<const uint16_t*>(cv);
   P.out = out;
+  P.lse = lse;
   P.B = sh.B;
   P.Hq = sh.Hq;
   P.Hkv = sh.Hkv;

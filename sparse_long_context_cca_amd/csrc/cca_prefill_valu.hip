@@ -24,8 +24,8 @@ template <int DT, int OT, int D>
 __global__ __launch_bounds__(256) void prefill_valu_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     const void* __restrict__ ck_, const void* __restrict__ cv_, void* __restrict__ out_, int m_cap,
-    const int32_t* __restrict__ q_start, const int32_t* __restrict__ q_len, int Hq, int Hkv, int Lq,
-    int Lk, int g, int w, float scale_log2) {
+    const int32_t* __restrict__ q_start, const int32_t* __restrict__ q_len, float* __restrict__ lse,
+    int Hq, int Hkv, int Lq, int Lk, int g, int w, float scale_log2) {
   typedef Elem<DT> E;
   typedef typename E::T T;
   constexpr int DH = D / 2;
@@ -140,16 +140,20 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
     const long orow = ((long)(b * Hq + h) * Lq + (t - qs)) * D + half * DH;
 #pragma unroll
     for (int e = 0; e < DH; ++e) EO::store(out, orow + e, acc[e] * inv);
+    // natural-log log-sum-exp of the row's scores, for a backward pass
+    if (lse != nullptr && half == 0)
+      lse[(long)(b * Hq + h) * Lq + (t - qs)] = (mrun + log2f(lrun)) * kLn2;
   }
 }
 
 template <int DT, int OT, int D>
 void launch_t(const void* q, const void* k, const void* v, const void* ck, const void* cv,
-              int m_cap, void* out, const Shape& sh, const RowRange& rr, hipStream_t s) {
+              int m_cap, void* out, const Shape& sh, const RowRange& rr, float* lse,
+              hipStream_t s) {
   dim3 grid((rr.Lq + kRows - 1) / kRows, sh.Hq, sh.B);
   const float scale_log2 = kLog2e / sqrtf((float)D);
   hipLaunchKernelGGL((prefill_valu_kernel<DT, OT, D>), grid, dim3(256), 0, s, q, k, v, ck, cv, out,
-                     m_cap, rr.q_start, rr.q_len, sh.Hq, sh.Hkv, rr.Lq, rr.Lk, sh.g, sh.w,
+                     m_cap, rr.q_start, rr.q_len, lse, sh.Hq, sh.Hkv, rr.Lq, rr.Lk, sh.g, sh.w,
                      scale_log2);
 }
 
@@ -157,16 +161,16 @@ void launch_t(const void* q, const void* k, const void* v, const void* ck, const
 
 hipError_t launch_prefill_valu(const void* q, const void* k, const void* v, const void* ck,
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
-                               const RowRange& rr, int dt, hipStream_t s) {
+                               const RowRange& rr, float* lse, int dt, hipStream_t s) {
   if (dt == 0) {
-    if (sh.d == 64) launch_t<0, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
-    else launch_t<0, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
+    if (sh.d == 64) launch_t<0, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, lse, s);
+    else launch_t<0, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, lse, s);
   } else if (out_dt == 1) {
-    if (sh.d == 64) launch_t<1, 1, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
-    else launch_t<1, 1, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
+    if (sh.d == 64) launch_t<1, 1, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, lse, s);
+    else launch_t<1, 1, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, lse, s);
   } else {
-    if (sh.d == 64) launch_t<1, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
-    else launch_t<1, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, s);
+    if (sh.d == 64) launch_t<1, 0, 64>(q, k, v, ck, cv, m_cap, out, sh, rr, lse, s);
+    else launch_t<1, 0, 128>(q, k, v, ck, cv, m_cap, out, sh, rr, lse, s);
   }
   return hipGetLastError();
 }
