@@ -4,11 +4,12 @@
 A step is one pass of the prefill hot path over the LLaMA-3.1-8B GQA workload
 (batch 1, 32 query / 8 kv heads, head dim 128, L = 131072, g = 16, w = 1024,
 bf16): cca_pool_core then cca_attn_prefill, inputs already resident in HBM.
-The decode workload (batch 8, 32/8 heads, 65536 cached tokens, 256 single-token
-steps) is timed in the same run and reported under "decode".
+The backward pass over the same workload (cca_attn_backward) and the decode
+workload (batch 8, 32/8 heads, 65536 cached tokens, 256 single-token steps) are
+timed in the same run and reported under "backward" and "decode".
 
 Prints ONE JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
---warmup W, --no-cpu (skip the CPU-oracle baseline), --no-decode.
+--warmup W, --no-cpu (skip the CPU-oracle baseline), --no-decode, --no-backward.
 """
 from __future__ import annotations
 
@@ -159,6 +160,49 @@ def cpu_oracle_baseline(cfg, q, k, v, budget_s=20.0):
     }
 
 
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector peak
+
+
+def bench_backward(cca, cfg, qd, kd, vd, steps=2, warmup=1):
+    """Backward pass over the prefill workload: forward with row statistics,
+    then cca_attn_backward timed with events over `steps` calls.  Algorithmic
+    FLOPs: 10*d per visible (query head, key) pair (the five products of a
+    flash-style backward: Q.K recomputed, dO.V, dS.K, dS^T.Q, P^T.dO)."""
+    B, Hq, Hkv, L, d, g, w = cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.g, cfg.w
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev).manual_seed(4242)
+    dout = torch.randn((B, Hq, L, d), generator=gen, device=dev).to(torch.bfloat16)
+    m = L // g
+    ck = torch.empty((B, Hkv, m, d), dtype=torch.bfloat16, device=dev)
+    cv = torch.empty_like(ck)
+    out = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
+    cca.cca_pool_core(qd, kd, vd, ck, cv, g)
+    cca.cca_attn_prefill_train(qd, kd, vd, ck, cv, out, lse, g, w)
+    dq = torch.empty((B, Hq, L, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, Hkv, L, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        cca.cca_attn_backward(qd, kd, vd, ck, cv, out, lse, dout, dq, dk, dv, ws, g, w)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        cca.cca_attn_backward(qd, kd, vd, ck, cv, out, lse, dout, dq, dk, dv, ws, g, w)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.isfinite(dq[0, :, -4:]).all() and torch.isfinite(dk[0, :, -4:]).all()
+    flops = 10.0 * d * B * Hq * visible_pairs(L, g, w)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"workload": cfg.name, "steps": steps, "ms_per_call": ms, "algorithmic_flops": flops,
+            "achieved_TFLOP_per_s": tflops, "bound": "alu", "peak": PEAK_FP32_VALU_TFLOPS,
+            "frac": tflops / PEAK_FP32_VALU_TFLOPS,
+            "note": "fp32 vector-ALU kernels; gradients fp32"}
+
+
 def bench_decode(cca, cfg, steps_timed=True):
     """256 sequential decode steps over a 65536-token cache; one timed region."""
     B, Hq, Hkv, d, g, w, L, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.g, cfg.w, cfg.L, cfg.decode_steps
@@ -251,6 +295,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one device-to-device copy of this many bytes (a counter "
                          "calibration reference for FETCH_SIZE/WRITE_SIZE)")
@@ -344,8 +389,13 @@ def main():
                  "traffic": measured_traffic("pool_gqa_L131072"),
                  "GB_per_s": pool_bytes(cfg) / (pool_ms * 1e-3) / 1e9 if pool_ms > 0 else None},
     }
+    del out, ck, cv
+    torch.cuda.empty_cache()
+    if not args.no_backward:
+        print("[bench] backward", file=sys.stderr, flush=True)
+        result["backward"] = bench_backward(cca, cfg, qd, kd, vd)
     if not args.no_decode:
-        del qd, kd, vd, out, ck, cv
+        del qd, kd, vd
         torch.cuda.empty_cache()
         print("[bench] decode", file=sys.stderr, flush=True)
         result["decode"] = bench_decode(cca, cca_inputs.CONFIGS[5])
