@@ -17,7 +17,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcca.so")
 
 SOURCES = ["cca_api.hip", "cca_pool.hip", "cca_prefill_valu.hip", "cca_prefill_mfma.hip",
-           "cca_decode.hip", "cca_backward.hip"]
+           "cca_decode.hip", "cca_backward.hip", "cca_backward_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

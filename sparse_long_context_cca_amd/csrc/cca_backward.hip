@@ -14,8 +14,10 @@
 // forward writes.  Pooling then sends the core gradients to the group's keys,
 // values and pooling query (see pool_backward_kernel).
 //
-// Kernels, in launch order (all arithmetic fp32 on the vector ALUs; inputs
-// fp32 or bf16; gradients fp32):
+// bf16 inputs take the matrix-core kernels of cca_backward_mfma.hip for steps
+// 1-4 (step 4 folded into its key-parallel kernel).  fp32 inputs take the
+// kernels below, in launch order (all arithmetic fp32 on the vector ALUs;
+// gradients fp32):
 //   1. row_dot_kernel       D_t = dO_t . o_t
 //   2. dq_kernel            row-parallel over each row's visible keys
 //   3. dkv_raw_kernel       key-parallel: raw key p is seen by rows p .. p+w-1
@@ -573,25 +575,37 @@ hipError_t launch_backward_t(const void* q, const void* k, const void* v, const 
   const int B = sh.B, Hq = sh.Hq, Hkv = sh.Hkv, L = sh.L, g = sh.g, w = sh.w;
   const int m = L / g;
   const float scale = 1.0f / sqrtf((float)D), c = kLog2e * scale;
-  float* Dv = ws;
-  float* dck = ws + (size_t)B * Hq * L;
-  float* dcv = dck + (size_t)B * Hkv * m * D;
+  // workspace: row statistics (2 floats per row), then dCK, dCV
   const long rows = (long)B * Hq * L;
-  hipLaunchKernelGGL((row_dot_kernel<DT, D>), dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s,
-                     out, dout, Dv, rows);
-  const int rb = (L + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL((dq_kernel<DT, D>), dim3(rb, Hq, B), dim3(256), 0, s, q, k, v, ck, cv, dout, lse,
-                     Dv, dq, m_cap, Hq, Hkv, L, g, w, c, scale);
-  hipLaunchKernelGGL((dkv_raw_kernel<DT, D>), dim3(rb, Hkv, B), dim3(256), 0, s, q, k, v, dout, lse,
-                     Dv, dk, dv, Hq, Hkv, L, w, c, scale);
+  float* dck = ws + 2 * (size_t)rows;
+  float* dcv = dck + (size_t)B * Hkv * m * D;
   if (m > 0) {
     const long nws = 2L * B * Hkv * m * D;
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<long>((nws + 255) / 256, 4096)), dim3(256),
                        0, s, dck, nws);
-    const int cb = (m + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int splits = (L + kCoreRowsPerSplit - 1) / kCoreRowsPerSplit;
-    hipLaunchKernelGGL((dcore_kernel<DT, D>), dim3(cb, splits, B * Hkv), dim3(256), 0, s, q, ck, cv, dout,
-                       lse, Dv, dck, dcv, m, m_cap, Hq, Hkv, L, g, w, c, scale);
+  }
+  if (DT == 1) {
+    // bf16: matrix-core kernels (cca_backward_mfma.hip)
+    const hipError_t e = launch_backward_mfma(q, k, v, ck, cv, m_cap, out, lse, dout, dq, dk, dv,
+                                              reinterpret_cast<float2*>(ws), dck, dcv, sh, s);
+    if (e != hipSuccess) return e;
+  } else {
+    float* Dv = ws;
+    hipLaunchKernelGGL((row_dot_kernel<DT, D>), dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s,
+                       out, dout, Dv, rows);
+    const int rb = (L + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL((dq_kernel<DT, D>), dim3(rb, Hq, B), dim3(256), 0, s, q, k, v, ck, cv, dout, lse,
+                       Dv, dq, m_cap, Hq, Hkv, L, g, w, c, scale);
+    hipLaunchKernelGGL((dkv_raw_kernel<DT, D>), dim3(rb, Hkv, B), dim3(256), 0, s, q, k, v, dout, lse,
+                       Dv, dk, dv, Hq, Hkv, L, w, c, scale);
+    if (m > 0) {
+      const int cb = (m + kRowsPerBlock - 1) / kRowsPerBlock;
+      const int splits = (L + kCoreRowsPerSplit - 1) / kCoreRowsPerSplit;
+      hipLaunchKernelGGL((dcore_kernel<DT, D>), dim3(cb, splits, B * Hkv), dim3(256), 0, s, q, ck, cv, dout,
+                         lse, Dv, dck, dcv, m, m_cap, Hq, Hkv, L, g, w, c, scale);
+    }
+  }
+  if (m > 0) {
     const long groups = (long)B * Hkv * m;
     const dim3 pg((unsigned)((groups + 3) / 4));
     switch (pool_mode) {
@@ -620,7 +634,7 @@ hipError_t launch_backward_t(const void* q, const void* k, const void* v, const 
 
 size_t backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g) {
   const size_t m = g > 0 ? (size_t)(L / g) : 0;
-  return ((size_t)B * Hq * L + 2 * (size_t)B * Hkv * m * d) * sizeof(float);
+  return (2 * (size_t)B * Hq * L + 2 * (size_t)B * Hkv * m * d) * sizeof(float);
 }
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* ck,

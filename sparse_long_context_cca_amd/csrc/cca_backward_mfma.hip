@@ -1,0 +1,683 @@
+// Backward pass of the CCA attention prefill on the gfx950 matrix cores (bf16
+// operands, fp32 accumulate and gradients).
+//
+// Gradients of the fused softmax (digest at digest.lyk-ai.com/posts/2412.12465,
+// "Method", fusion formula; the pages fine-tune with CCA attention in place:
+// paper card at atlas.scime.ai, summary; rebuttal at paperhub.cn, answer on the
+// fine-tuning setting).  For row t with visible keys k (cores, then raw), score
+// S = q_t . key_k / sqrt(d), P = softmax(S) recomputed from the row's
+// log-sum-exp, dP = dO_t . value_k and D_t = dO_t . o_t:
+//   dS = P (dP - D_t)
+//   dq_t = sum_k dS key_k / sqrt(d)                      (dq_mfma_kernel)
+//   dkey_k = sum_t dS q_t / sqrt(d), dvalue_k = sum_t P dO_t   (dkv_mfma_kernel)
+// Kernels, in launch order:
+//   1. row_stats_kernel  per row {lse * log2(e), D_t}
+//   2. dq_mfma_kernel    row-parallel, the forward's work decomposition: per
+//                        64-key tile S^T = K.Q^T and dP^T = V.dO^T (K, V rows
+//                        from LDS, Q and dO fragments in registers), then
+//                        dQ^T += K^T.dS^T with K^T through transposing reads
+//   3. dkv_mfma_kernel   key-parallel: a workgroup owns 128 keys (raw
+//                        positions, or cores) of one kv head, each pair of
+//                        waves 32 of them with their K and V fragments in
+//                        registers, and walks the rows that see them for every
+//                        query head of the group: S = Q.K^T, dP = dO.V^T (Q,
+//                        dO rows from LDS), dV^T += dO^T.P and dK^T += Q^T.dS
+//                        (dO^T, Q^T through transposing reads).  Raw keys get
+//                        plain stores; core rows are split over workgroups and
+//                        meet by atomic adds in an fp32 workspace.
+// The pooling share of the gradients is added afterwards by the pooling
+// backward of cca_backward.hip.
+#include <algorithm>
+#include <type_traits>
+
+#include "cca_device.hpp"
+#include "cca_internal.hpp"
+#include "cca_lds.hpp"
+
+namespace cca {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTileRows = 64;    // keys per tile (dQ), rows per tile (dK dV)
+constexpr int kKeysPerUnit = 128;  // keys per dK dV workgroup (4 wave pairs x 32)
+constexpr int kCoreSplit = 4096;   // rows per core unit (absolute, aligned splits)
+
+// ------------------------------------------------------------- 1. statistics
+
+// stats[row] = {lse[row] * log2(e), dO_row . O_row}; 16 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* __restrict__ out,
+                                                        const uint16_t* __restrict__ dout,
+                                                        const float* __restrict__ lse,
+                                                        float2* __restrict__ stats, long rows) {
+  constexpr int LPR = 16, EPL = D / LPR;
+  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPR;
+  const int part = threadIdx.x % LPR;
+  const bool valid = row < rows;
+  float acc = 0.f;
+  if (valid) {
+    const uint16_t* o = out + row * D + part * EPL;
+    const uint16_t* gg = dout + row * D + part * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = fmaf(bf16_to_f32(o[e]), bf16_to_f32(gg[e]), acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (valid && part == 0) stats[row] = make_float2(lse[row] * kLog2e, acc);
+}
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// ------------------------------------------------------------------ 2. dQ
+
+struct DqParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* ck;
+  const uint16_t* cv;
+  const uint16_t* dout;
+  const float2* stats;
+  float* dq;
+  int B, Hq, Hkv, L, g, w, m_cap;
+  int G, Hw, RP;     // heads per workgroup, rows per head per workgroup
+  int nPB, nHG, U;   // position blocks, head groups per kv head, units
+  int xcd;
+  float c, scale;
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dq_mfma_kernel(DqParams P) {
+  constexpr int NW = 8, kThreads = 64 * NW;
+  constexpr int KS = D / 16, DB = D / 32, CPR = D / 8;
+  typedef BothWaysTile<D> KT;          // K: row reads (S) and transposing reads (dQ)
+  constexpr int VRow = D * 2 + 16;     // V: row reads only; one chunk of padding per row
+  constexpr int VBytes = kTileRows * VRow;
+  static_assert(VBytes % 1024 == 0, "V tile is a whole number of wave loads");
+  constexpr int NKI = KT::kLoads, NVI = VBytes / 1024, NL = NKI + NVI;
+  constexpr int NLW = (NL + NW - 1) / NW, NLMIN = NL / NW;
+  __shared__ __attribute__((aligned(16))) char lds[3 * (KT::kBytes + VBytes)];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int j = lane & 31, hh = lane >> 5;
+
+  // ---- rows: longest first, all units of one kv head on one XCD when possible
+  const long bid = blockIdx.x;
+  int pb, u;
+  if (P.xcd) {
+    const int per = P.U / 8;
+    const long slot = bid >> 3;
+    const int x = (int)(bid & 7);
+    pb = P.nPB - 1 - (int)(slot / per);
+    u = x * per + (int)(slot % per);
+  } else {
+    pb = P.nPB - 1 - (int)(bid / P.U);
+    u = (int)(bid % P.U);
+  }
+  const int kvp = u / P.nHG, hg = u % P.nHG;
+  const int b = kvp / P.Hkv;
+  const int g = P.g, w = P.w, L = P.L;
+  const int h = (kvp % P.Hkv) * P.G + hg * P.Hw + (wave % P.Hw);
+  const int row0 = pb * P.RP + 32 * (wave / P.Hw);
+  const int P_lo = pb * P.RP;
+  const int P_hi = min(L - 1, P_lo + P.RP - 1);
+  const int t_raw = row0 + j;
+  const int t = min(t_raw, L - 1);
+  const int my_nc = n_core(t, g, w), my_lo = win_lo(t, w);
+  const int w_lo = uni(min(row0, L - 1)), w_hi = uni(min(row0 + 31, L - 1));
+  const int wnc_lo = uni(n_core(w_lo, g, w)), wnc_hi = uni(n_core(w_hi, g, w));
+  const int wlo_lo = uni(win_lo(w_lo, w)), wlo_hi = uni(win_lo(w_hi, w));
+  const int nc_hi = uni(n_core(P_hi, g, w));
+  const int n_ct = (nc_hi + kTileRows - 1) / kTileRows;
+  const int r0 = win_lo(P_lo, w) & ~(kTileRows - 1);
+  const int n_rt = (P_hi - r0) / kTileRows + 1;
+  const int n_tiles = uni(n_ct + n_rt);
+
+  const uint16_t* kbase = P.k + (long)kvp * L * D;
+  const uint16_t* vbase = P.v + (long)kvp * L * D;
+  const uint16_t* ckbase = P.ck + (long)kvp * P.m_cap * D;
+  const uint16_t* cvbase = P.cv + (long)kvp * P.m_cap * D;
+
+  // ---- this lane's row: Q and dO fragments (B operands), statistics
+  const long grow = ((long)b * P.Hq + h) * L + t;
+  bf16x8 qf[KS], gf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qf[ks] = *reinterpret_cast<const bf16x8*>(P.q + grow * D + 16 * ks + 8 * hh);
+    gf[ks] = *reinterpret_cast<const bf16x8*>(P.dout + grow * D + 16 * ks + 8 * hh);
+  }
+  const float2 st = P.stats[grow];
+  const float lse2 = st.x, Dt = st.y;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(gf[ks]));
+  asm volatile("" ::"v"(lse2), "v"(Dt));
+
+  // ---- tile loaders: load index li < NKI fills the K tile, the rest the V tile
+  int soff[NLW];
+#pragma unroll
+  for (int i = 0; i < NLW; ++i) {
+    const int li = wave + NW * i;
+    if (li < NKI) {
+      soff[i] = KT::src_offset(li * 64 + lane);
+    } else {
+      const int slot = (li - NKI) * 64 + lane;
+      const int row = slot / (CPR + 1), chunk = slot % (CPR + 1);
+      soff[i] = chunk < CPR ? (row * D + 8 * chunk) * 2 : 0x40000000;
+    }
+  }
+  auto tile_core = [&](int it) { return it < n_ct; };
+  auto tile_base = [&](int it) { return it < n_ct ? it * kTileRows : r0 + (it - n_ct) * kTileRows; };
+  auto kbuf = [&](int s) { return lds + s * KT::kBytes; };
+  auto vbuf = [&](int s) { return lds + 3 * KT::kBytes + s * VBytes; };
+  auto load_tile = [&](int slot, int it) {
+    const bool core = tile_core(it);
+    const int base = tile_base(it);
+    const int lim = core ? nc_hi : P_hi + 1;
+    const int nbytes = max(0, min(kTileRows, lim - base)) * D * 2;
+    const long off = (long)base * D;
+    const u32x4 rk = buffer_desc((core ? ckbase : kbase) + off, nbytes);
+    const u32x4 rv = buffer_desc((core ? cvbase : vbase) + off, nbytes);
+    const uint32_t kb = lds_addr(kbuf(slot)), vb = lds_addr(vbuf(slot));
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int li = wave + NW * i;
+      if (li < NKI) lds_dma16(rk, kb + li * 1024, soff[i]);
+      else if (li < NL) lds_dma16(rv, vb + (li - NKI) * 1024, soff[i]);
+    }
+  };
+  auto sync_stage = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NLMIN) : "memory");
+  };
+
+  // LDS addresses: row read of K row 32kb + j (A operand of S^T), of V row;
+  // transposing read of K (A operand of dQ^T): lane s of a 16-lane group at
+  // row 16cc + 8x + 4hh + s/4, dims 32db + 16((lane/16)%2) + 4(s%4) .. +3
+  const int krow_off = KT::row_off(j) + 16 * hh;
+  const int vrow_off = j * VRow + 16 * hh;
+  const int s16 = lane & 15;
+  const int ktr_off = hh * KT::kGroup + (s16 >> 2) * KT::kRow + 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
+
+  auto tile_full = [&](int it) {
+    const int base = tile_base(it);
+    return tile_core(it) ? base + kTileRows <= wnc_lo : (base >= wlo_hi && base + kTileRows - 1 <= w_lo);
+  };
+  auto tile_seen = [&](int it) {  // does any row of the wave see a key of the tile?
+    const int base = tile_base(it);
+    return tile_core(it) ? base < wnc_hi : (base + kTileRows - 1 >= wlo_lo && base <= w_hi);
+  };
+
+  f32x16 dqt[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
+  const float c = P.c;
+
+  load_tile(0, 0);
+  load_tile(1, 1);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NLMIN) : "memory");
+  int slot = 0;
+  for (int it = 0; it < n_tiles; ++it) {
+    const int nslot = slot == 0 ? 2 : slot - 1;  // (it + 2) % 3
+    load_tile(nslot, it + 2);
+    if (tile_seen(it)) {
+      const char* kt = kbuf(slot);
+      const char* vt = vbuf(slot);
+      f32x16 sx[2], dpx[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sx[kb][r] = dpx[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + krow_off + kb * 8 * KT::kGroup + 32 * ks);
+          sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sx[kb], 0, 0, 0);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + vrow_off + kb * 32 * VRow + 32 * ks);
+          dpx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gf[ks], dpx[kb], 0, 0, 0);
+        }
+      // P and dS of this lane's row; key kk = 32kb + 8(r/4) + 4hh + r%4
+      const bool full = tile_full(it);
+      const int base = tile_base(it);
+      const bool core = tile_core(it);
+      const int lo_rel = core ? 0 : my_lo - base;
+      const int hi_rel = core ? my_nc - 1 - base : t - base;
+      const unsigned span = (unsigned)(hi_rel - lo_rel);
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float ds2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int kk = 32 * kb + 8 * ((r + x) >> 2) + 4 * hh + ((r + x) & 3);
+            const bool vis = full || (hi_rel >= lo_rel && (unsigned)(kk - lo_rel) <= span);
+            const float p = __builtin_amdgcn_exp2f(fmaf(sx[kb][r + x], c, -lse2));
+            ds2[x] = vis ? p * (dpx[kb][r + x] - Dt) : 0.f;
+          }
+          const int cc = 2 * kb + (r >> 3), e = r & 7;
+          dsb[cc][e] = static_cast<__bf16>(ds2[0]);
+          dsb[cc][e + 1] = static_cast<__bf16>(ds2[1]);
+        }
+      // dQ^T += K^T . dS^T
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const char* p0 = kt + ktr_off + (4 * cc) * KT::kGroup + 64 * db;
+          const bf16x4 x0 = lds_read_tr16(p0);
+          const bf16x4 x1 = lds_read_tr16(p0 + 2 * KT::kGroup);
+          const bf16x8 a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[cc], dqt[db], 0, 0, 0);
+        }
+    }
+    slot = slot == 2 ? 0 : slot + 1;
+    sync_stage();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
+  if (t_raw < L) {
+    float* out = P.dq + (((long)b * P.Hq + h) * L + t_raw) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * hh;
+        *reinterpret_cast<float4*>(out + d0) =
+            make_float4(dqt[db][4 * q4] * P.scale, dqt[db][4 * q4 + 1] * P.scale,
+                        dqt[db][4 * q4 + 2] * P.scale, dqt[db][4 * q4 + 3] * P.scale);
+      }
+  }
+}
+
+// --------------------------------------------------------------- 3. dK, dV
+
+struct DkvParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* ck;
+  const uint16_t* cv;
+  const uint16_t* dout;
+  const float2* stats;
+  float* dk;   // raw-key gradients [B,Hkv,L,d]
+  float* dv;
+  float* dck;  // core gradients [B,Hkv,m,d], accumulated with atomic adds
+  float* dcv;
+  int B, Hq, Hkv, L, g, w, m, m_cap, G;
+  int nCB, nSplit, nRB, UP;  // core blocks, row splits, raw blocks, units per (b, kv head)
+  int xcd;
+  float c, scale;
+};
+
+// A workgroup of 8 waves owns 128 keys.  Waves 2p and 2p+1 share keys
+// 32p .. 32p+31: per 64-row tile each computes S and dP for one half of the
+// rows, both publish P and dS in LDS, and each accumulates dV^T and dK^T
+// over all 64 rows for one half of the head dims.  (One wave per key block
+// would need some 330 registers; split this way a wave fits in 256, two per
+// SIMD.)
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dkv_mfma_kernel(DkvParams P) {
+  constexpr int NW = 8;
+  constexpr int KS = D / 16, DB = D / 32, DBH = DB / 2;
+  typedef BothWaysTile<D> RT;  // Q and dO tiles: row reads and transposing reads
+  // The row statistics of a tile (64 x 8 bytes) sit in the Q tile's unused tail.
+  static_assert(RT::kBytes - RT::kBytesUsed >= 512, "room for the row statistics");
+  constexpr int QTailLanes = (RT::kBytesUsed - (RT::kLoads - 1) * 1024) / 16;  // live lanes of Q's last load
+  constexpr int SlotBytes = 2 * RT::kBytes;
+  constexpr int XBytes = NW * 4 * 1024;  // per wave: P and dS fragments of two k-steps
+  constexpr int NL = 2 * RT::kLoads + 1;
+  constexpr int NLW = (NL + NW - 1) / NW, NLMIN = NL / NW;
+  __shared__ __attribute__((aligned(16))) char lds[3 * SlotBytes + XBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int pair = wave >> 1, half = wave & 1;
+  const int i32 = lane & 31, hh = lane >> 5;
+  const int g = P.g, w = P.w, L = P.L;
+
+  // ---- unit: core units (split-major) first, then raw-key units
+  const long bid = blockIdx.x;
+  const int BH = P.B * P.Hkv;
+  int kvp, u;
+  if (P.xcd) {
+    const int hpx = BH / 8;
+    const long q = bid >> 3;
+    kvp = (int)(bid & 7) * hpx + (int)(q % hpx);
+    u = (int)(q / hpx);
+  } else {
+    kvp = (int)(bid % BH);
+    u = (int)(bid / BH);
+  }
+  const int b = kvp / P.Hkv;
+  const bool core = u < P.nCB * P.nSplit;
+  int key_lo, key_lim, t_lo, t_end;
+  if (core) {
+    const int split = u / P.nCB, cb = u % P.nCB;
+    key_lo = cb * kKeysPerUnit;
+    key_lim = P.m;
+    t_lo = max((key_lo + 1) * g + w - 1, split * kCoreSplit);
+    t_end = min(L, (split + 1) * kCoreSplit) - 1;
+  } else {
+    const int rb = u - P.nCB * P.nSplit;
+    key_lo = rb * kKeysPerUnit;
+    key_lim = L;
+    t_lo = key_lo;
+    t_end = min(L - 1, key_lo + kKeysPerUnit - 1 + w - 1);
+  }
+  t_lo = uni(t_lo);
+  t_end = uni(t_end);
+  if (t_lo > t_end) return;  // nothing sees these keys in this split
+  const int n_rt = (t_end - t_lo) / kTileRows + 1;
+  const int n_it = P.G * n_rt;
+
+  // ---- this pair's keys k0 .. k0+31 and this lane's key
+  const int k0 = key_lo + 32 * pair;
+  const int key = k0 + i32;
+  const bool key_ok = key < key_lim;
+  // rows that see this lane's key: [lo, hi] (empty when hi < lo)
+  int lo, hi;
+  if (core) {
+    lo = (key + 1) * g + w - 1;
+    hi = key_ok ? t_end : lo - 1;
+  } else {
+    lo = key;
+    hi = key_ok ? min(key + w - 1, t_end) : lo - 1;
+  }
+  const bool wave_keys_ok = k0 + 31 < key_lim;
+  const int lo_max = core ? (k0 + 32) * g + w - 1 : k0 + 31;
+  const int hi_min = core ? t_end : min(k0 + w - 1, t_end);
+
+  const long kvrow = (long)kvp;
+  const uint16_t* kb_ = core ? P.ck + kvrow * P.m_cap * D : P.k + kvrow * L * D;
+  const uint16_t* vb_ = core ? P.cv + kvrow * P.m_cap * D : P.v + kvrow * L * D;
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (key_ok) {
+      kf[ks] = *reinterpret_cast<const bf16x8*>(kb_ + (long)key * D + 16 * ks + 8 * hh);
+      vf[ks] = *reinterpret_cast<const bf16x8*>(vb_ + (long)key * D + 16 * ks + 8 * hh);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[ks][e] = vf[ks][e] = static_cast<__bf16>(0.0f);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
+
+  // ---- tile loaders: load index li < RT::kLoads fills Q, then dO, then the statistics
+  int soff[NLW];
+#pragma unroll
+  for (int i = 0; i < NLW; ++i) {
+    const int li = wave + NW * i;
+    if (li < RT::kLoads) soff[i] = RT::src_offset(li * 64 + lane);
+    else if (li < 2 * RT::kLoads) soff[i] = RT::src_offset((li - RT::kLoads) * 64 + lane);
+    else soff[i] = 16 * lane;
+  }
+  auto qbuf = [&](int s) { return lds + s * SlotBytes; };
+  auto gbuf = [&](int s) { return lds + s * SlotBytes + RT::kBytes; };
+  auto sbuf = [&](int s) { return lds + s * SlotBytes + RT::kBytesUsed; };
+  char* xbuf = lds + 3 * SlotBytes;
+  auto load_tile = [&](int slot, int it) {
+    const int hg = it / n_rt, tile = it % n_rt;
+    const int t0 = t_lo + tile * kTileRows;
+    const int nr = it < n_it ? max(0, min(kTileRows, t_end + 1 - t0)) : 0;
+    const long row = ((long)b * P.Hq + (long)(kvp % P.Hkv) * P.G + hg) * L + t0;
+    const u32x4 rq = buffer_desc(P.q + row * D, nr * D * 2);
+    const u32x4 rg = buffer_desc(P.dout + row * D, nr * D * 2);
+    const u32x4 rs = buffer_desc(P.stats + row, nr * 8);
+    const uint32_t qa = lds_addr(qbuf(slot)), ga = lds_addr(gbuf(slot)), sa = lds_addr(sbuf(slot));
+    // load li = wave + NW i: which array it fills is uniform (a scalar select).
+    // Q's last load leaves the tail (the statistics' place) alone; the
+    // statistics load writes 512 bytes.
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int li = wave + NW * i;
+      if (NW * i + NW <= RT::kLoads - 1) {
+        lds_dma16(rq, qa + li * 1024, soff[i]);
+      } else if (NW * i >= RT::kLoads && NW * i + NW <= 2 * RT::kLoads) {
+        lds_dma16(rg, ga + (li - RT::kLoads) * 1024, soff[i]);
+      } else if (li < NL) {
+        const bool isq = li < RT::kLoads, isg = li < 2 * RT::kLoads;
+        const u32x4 r = isq ? rq : (isg ? rg : rs);
+        const uint32_t dst = isq ? qa + li * 1024 : (isg ? ga + (li - RT::kLoads) * 1024 : sa);
+        const int live = li == RT::kLoads - 1 ? QTailLanes : (isg ? 64 : 32);
+        if (lane < live) lds_dma16(r, dst, soff[i]);
+      }
+    }
+  };
+  auto sync_stage = [&]() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NLMIN) : "memory");
+  };
+
+  // LDS addresses: row read of Q / dO row 32 half + i32 (A operand of S, dP);
+  // transposing read (A operand of dV^T, dK^T): lane s of a 16-lane group at
+  // row 16cc + 8x + 4hh + s/4, dims 32db + 16((lane/16)%2) + 4(s%4) .. +3
+  const int rrow_off = RT::row_off(32 * half + i32) + 16 * hh;
+  const int s16 = lane & 15;
+  const int rtr_off = hh * RT::kGroup + (s16 >> 2) * RT::kRow + 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) +
+                      64 * DBH * half;
+  char* xmine = xbuf + wave * 4096 + 16 * lane;           // [frag][lane] of this wave
+  const char* xpair = xbuf + (2 * pair) * 4096 + 16 * lane;  // the pair's first wave
+
+  f32x16 dkt[DBH], dvt[DBH];
+#pragma unroll
+  for (int db = 0; db < DBH; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
+  const float c = P.c;
+
+  load_tile(0, 0);
+  load_tile(1, 1);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NLMIN) : "memory");
+  int slot = 0;
+  int tile = 0;  // it % n_rt
+  for (int it = 0; it < n_it; ++it) {
+    const int nslot = slot == 0 ? 2 : slot - 1;
+    load_tile(nslot, it + 2);
+    const int t0 = t_lo + tile * kTileRows;
+    const int tw = t0 + 32 * half;  // first row of this wave's half
+    const char* qt = qbuf(slot);
+    const char* gt = gbuf(slot);
+    const char* sta = sbuf(slot);
+    // S, dP over this wave's 32 rows; register r is row tw + 8(r/4) + 4hh + r%4
+    f32x16 sx, dpx;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sx[r] = dpx[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + rrow_off + 32 * ks);
+      sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sx, 0, 0, 0);
+      const bf16x8 ag = *reinterpret_cast<const bf16x8*>(gt + rrow_off + 32 * ks);
+      dpx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[ks], dpx, 0, 0, 0);
+    }
+    // P and dS (bf16 fragments, k-steps 2 half and 2 half + 1) into LDS
+    const bool full = wave_keys_ok && tw >= lo_max && tw + 31 <= hi_min;
+    auto publish = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const unsigned span = (unsigned)(hi - lo);
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int rr = 32 * half + 8 * q4 + 4 * hh;  // tile row of this lane's first of 4
+        const float4 s01 = *reinterpret_cast<const float4*>(sta + rr * 8);
+        const float4 s23 = *reinterpret_cast<const float4*>(sta + rr * 8 + 16);
+        const float l2[4] = {s01.x, s01.z, s23.x, s23.z};
+        const float dd[4] = {s01.y, s01.w, s23.y, s23.w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int r = 4 * q4 + x;
+          float p = __builtin_amdgcn_exp2f(fmaf(sx[r], c, -l2[x]));
+          if (MASK) {
+            const bool vis = hi >= lo && (unsigned)(t0 + rr + x - lo) <= span;
+            p = vis ? p : 0.f;
+          }
+          pb[q4 >> 1][4 * (q4 & 1) + x] = static_cast<__bf16>(p);
+          dsb[q4 >> 1][4 * (q4 & 1) + x] = static_cast<__bf16>(p * (dpx[r] - dd[x]));
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        *reinterpret_cast<bf16x8*>(xmine + h2 * 1024) = pb[h2];
+        *reinterpret_cast<bf16x8*>(xmine + (2 + h2) * 1024) = dsb[h2];
+      }
+    };
+    if (full) publish(std::false_type{});
+    else publish(std::true_type{});
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // dV^T += dO^T . P and dK^T += Q^T . dS over the 64 rows, this wave's dims
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const char* xf = xpair + (cc >> 1) * 4096 + (cc & 1) * 1024;
+      const bf16x8 pbf = *reinterpret_cast<const bf16x8*>(xf);
+      const bf16x8 dsf = *reinterpret_cast<const bf16x8*>(xf + 2048);
+#pragma unroll
+      for (int db = 0; db < DBH; ++db) {
+        const int o = rtr_off + (4 * cc) * RT::kGroup + 64 * db;
+        const bf16x4 g0 = lds_read_tr16(gt + o), g1 = lds_read_tr16(gt + o + 2 * RT::kGroup);
+        const bf16x8 ag = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pbf, dvt[db], 0, 0, 0);
+        const bf16x4 q0 = lds_read_tr16(qt + o), q1 = lds_read_tr16(qt + o + 2 * RT::kGroup);
+        const bf16x8 aq = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf, dkt[db], 0, 0, 0);
+      }
+    }
+    slot = slot == 2 ? 0 : slot + 1;
+    tile = tile + 1 == n_rt ? 0 : tile + 1;
+    sync_stage();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // lane holds dims 32(DBH half + db) + 8(r/4) + 4hh + r%4 of its key
+  if (!key_ok) return;
+  if (!core) {
+    const long orow = ((long)kvp * L + key) * D;
+#pragma unroll
+    for (int db = 0; db < DBH; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * (DBH * half + db) + 8 * q4 + 4 * hh;
+        *reinterpret_cast<float4*>(P.dk + orow + d0) =
+            make_float4(dkt[db][4 * q4] * P.scale, dkt[db][4 * q4 + 1] * P.scale,
+                        dkt[db][4 * q4 + 2] * P.scale, dkt[db][4 * q4 + 3] * P.scale);
+        *reinterpret_cast<float4*>(P.dv + orow + d0) =
+            make_float4(dvt[db][4 * q4], dvt[db][4 * q4 + 1], dvt[db][4 * q4 + 2], dvt[db][4 * q4 + 3]);
+      }
+  } else {
+    const long orow = ((long)kvp * P.m + key) * D;
+#pragma unroll
+    for (int db = 0; db < DBH; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * (DBH * half + db) + 8 * (r >> 2) + 4 * hh + (r & 3);
+        atomicAdd(P.dck + orow + d, dkt[db][r] * P.scale);
+        atomicAdd(P.dcv + orow + d, dvt[db][r]);
+      }
+  }
+}
+
+constexpr int kDqWaves = 8;
+
+int gcd_int(int a, int b) {
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+template <int D>
+hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck, const void* cv,
+                    int m_cap, const void* out, const float* lse, const void* dout, float* dq,
+                    float* dk, float* dv, float2* stats, float* dck, float* dcv, const Shape& sh,
+                    hipStream_t s) {
+  const int B = sh.B, Hq = sh.Hq, Hkv = sh.Hkv, L = sh.L, g = sh.g, w = sh.w;
+  const int m = L / g;
+  const float scale = 1.0f / sqrtf((float)D), c = kLog2e * scale;
+  const long rows = (long)B * Hq * L;
+  hipLaunchKernelGGL((row_stats_kernel<D>), dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, stats, rows);
+
+  DqParams Q;
+  Q.q = static_cast<const uint16_t*>(q);
+  Q.k = static_cast<const uint16_t*>(k);
+  Q.v = static_cast<const uint16_t*>(v);
+  Q.ck = static_cast<const uint16_t*>(ck);
+  Q.cv = static_cast<const uint16_t*>(cv);
+  Q.dout = static_cast<const uint16_t*>(dout);
+  Q.stats = stats;
+  Q.dq = dq;
+  Q.B = B;
+  Q.Hq = Hq;
+  Q.Hkv = Hkv;
+  Q.L = L;
+  Q.g = g;
+  Q.w = w;
+  Q.m_cap = m_cap;
+  Q.G = sh.G();
+  Q.Hw = gcd_int(Q.G, kDqWaves);
+  Q.RP = 32 * (kDqWaves / Q.Hw);
+  Q.nPB = (L + Q.RP - 1) / Q.RP;
+  Q.nHG = Q.G / Q.Hw;
+  Q.U = B * Hkv * Q.nHG;
+  Q.xcd = (Q.U % 8 == 0) ? 1 : 0;
+  Q.c = c;
+  Q.scale = scale;
+  const long qblocks = (long)Q.nPB * Q.U;
+  if (qblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3((unsigned)qblocks), dim3(64 * kDqWaves), 0, s, Q);
+
+  DkvParams K;
+  K.q = Q.q;
+  K.k = Q.k;
+  K.v = Q.v;
+  K.ck = Q.ck;
+  K.cv = Q.cv;
+  K.dout = Q.dout;
+  K.stats = stats;
+  K.dk = dk;
+  K.dv = dv;
+  K.dck = dck;
+  K.dcv = dcv;
+  K.B = B;
+  K.Hq = Hq;
+  K.Hkv = Hkv;
+  K.L = L;
+  K.g = g;
+  K.w = w;
+  K.m = m;
+  K.m_cap = m_cap;
+  K.G = sh.G();
+  K.nCB = (m + kKeysPerUnit - 1) / kKeysPerUnit;
+  K.nSplit = (L + kCoreSplit - 1) / kCoreSplit;
+  K.nRB = (L + kKeysPerUnit - 1) / kKeysPerUnit;
+  K.UP = K.nCB * K.nSplit + K.nRB;
+  K.xcd = ((B * Hkv) % 8 == 0) ? 1 : 0;
+  K.c = c;
+  K.scale = scale;
+  const long kblocks = (long)K.UP * B * Hkv;
+  if (kblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((dkv_mfma_kernel<D>), dim3((unsigned)kblocks), dim3(512), 0, s, K);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_mfma(const void* q, const void* k, const void* v, const void* ck,
+                                const void* cv, int m_cap, const void* out, const float* lse,
+                                const void* dout, float* dq, float* dk, float* dv, float2* stats,
+                                float* dck, float* dcv, const Shape& sh, hipStream_t s) {
+  if (sh.d == 64)
+    return launch_t<64>(q, k, v, ck, cv, m_cap, out, lse, dout, dq, dk, dv, stats, dck, dcv, sh, s);
+  return launch_t<128>(q, k, v, ck, cv, m_cap, out, lse, dout, dq, dk, dv, stats, dck, dcv, sh, s);
+}
+
+}  // namespace cca

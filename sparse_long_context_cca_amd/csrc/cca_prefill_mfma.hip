@@ -35,12 +35,10 @@
 // tiles ahead (buffer loads whose range check zero-fills keys past the end).
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
+#include "cca_lds.hpp"
 
 namespace cca {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;       // keys per tile
 constexpr float kLazyLog2 = 8.0f;  // rescale threshold of the running max, log2 units
@@ -73,45 +71,6 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// 32-bit LDS address of a pointer into a __shared__ array.  (Address-space
-// casts live in plain functions: inside the kernel template they have no host
-// form and would drop the host-side launch stub.)
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
-// lane s points at 4 consecutive 16-bit elements X_s[0..3]; lane i receives
-// X_{4e + (i%16)/4}[i % 4] for e = 0..3.
-__device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)p);
-}
-
-// Buffer resource over `nbytes` bytes from `base` (raw, no stride); reads past
-// the range return zeros.  Every word is uniform (scalar registers).
-__device__ __forceinline__ u32x4 buffer_desc(const void* base, int nbytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  u32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu;
-  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)nbytes);
-  r[3] = 0x00020000u;
-  return r;
-}
-
-// One wave load from a buffer straight into LDS: lane i's 16 bytes (from byte
-// voffset of the buffer) land at LDS address m0 + 16 i; m0 is uniform.  Issued
-// as inline assembly so that the compiler does not see an LDS write: it would
-// otherwise make every later LDS read wait for all such loads in flight.  The
-// caller therefore orders these loads itself (a vmcnt wait and a barrier
-// before the data are read, and before the kernel ends).
-__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t m0, int voffset) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rsrc), "{m0}"(m0));
 }
 
 // Two waves per SIMD (the accumulators stay in arch VGPRs, 256 per wave) so
