@@ -93,6 +93,42 @@ def attn_backward(Q, K, V, CK, CV, g: int, w: int, dO):
     return dQ, dK, dV, dCK, dCV
 
 
+def attn_backward_rows(Q, K, V, CK, CV, g: int, w: int, dO, rows):
+    """Step 1 restricted to the query rows ``rows`` (every batch and head).
+
+    The same chain rule as ``attn_backward``, with the G query heads of a kv
+    head handled together by small matrix products, for long sequences where
+    only some rows are wanted.  Returns dQ [B,Hq,len(rows),d] of those rows
+    and the contributions of those rows alone to dK, dV [B,Hkv,L,d] and dCK,
+    dCV [B,Hkv,m,d] (fp64); over all rows it is ``attn_backward``.
+    """
+    B, Hq, L, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    K, V, CK, CV = (_f64(x) for x in (K, V, CK, CV))
+    scale = _scale(d)
+    rows = list(rows)
+    dQ = np.zeros((B, Hq, len(rows), d))
+    dK, dV = np.zeros_like(K), np.zeros_like(V)
+    dCK, dCV = np.zeros_like(CK), np.zeros_like(CV)
+    T = (0, 1, 3, 2)
+    for i, t in enumerate(rows):
+        nc, lo = n_core(t, g, w), win_lo(t, w)
+        q = _f64(Q[:, :, t]).reshape(B, Hkv, G, d)       # head h -> kv head h // G
+        go = _f64(dO[:, :, t]).reshape(B, Hkv, G, d)
+        ck, cv = CK[:, :, :nc], CV[:, :, :nc]
+        kw, vw = K[:, :, lo : t + 1], V[:, :, lo : t + 1]
+        p = _softmax(np.concatenate([q @ ck.transpose(T), q @ kw.transpose(T)], axis=-1) * scale)
+        dp = np.concatenate([go @ cv.transpose(T), go @ vw.transpose(T)], axis=-1)
+        ds = _softmax_backward(p, dp)                      # [B,Hkv,G,nc + window]
+        dQ[:, :, i] = ((ds[..., :nc] @ ck + ds[..., nc:] @ kw) * scale).reshape(B, Hq, d)
+        dCK[:, :, :nc] += ds[..., :nc].transpose(T) @ q * scale   # summed over the G heads
+        dCV[:, :, :nc] += p[..., :nc].transpose(T) @ go
+        dK[:, :, lo : t + 1] += ds[..., nc:].transpose(T) @ q * scale
+        dV[:, :, lo : t + 1] += p[..., nc:].transpose(T) @ go
+    return dQ, dK, dV, dCK, dCV
+
+
 def pool_backward(Q, K, V, g: int, dCK, dCV, mode: str = "softmax"):
     """Gradients of pooling (step 2) for upstream dCK, dCV [B,Hkv,m,d].
 
@@ -184,4 +220,4 @@ def row_lse(Q, K, CK, g: int, w: int):
     return out
 
 
-__all__ = ["attn_backward", "pool_backward", "backward", "loss", "row_lse"]
+__all__ = ["attn_backward", "attn_backward_rows", "pool_backward", "backward", "loss", "row_lse"]

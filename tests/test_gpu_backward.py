@@ -108,3 +108,63 @@ def test_backward_is_deterministic_where_no_atomics():
     a = run("bf16", 1, 4, 2, 300, 128, 16, 32, cca.CCA_POOL_MEAN, seed=5)[0]
     b = run("bf16", 1, 4, 2, 300, 128, 16, 32, cca.CCA_POOL_MEAN, seed=5)[0]
     assert torch.equal(a[0], b[0])
+
+
+def test_backward_full_size_sampled():
+    """The 128K GQA workload (B1, 32/8 heads, d128, g16, w1024) at full size, in
+    the launch configuration the benchmark times.  Checked against the oracle
+    for one kv head (its 4 query heads) where every contribution can be
+    summed cheaply: dq at every row of the last w + 3g positions and at rows
+    deep in the sequence that end no group; dk, dv at positions of the last
+    groups, whose raw-key rows and whose core's rows (the pooling share) all
+    lie in that range."""
+    cfg = cca_inputs.CONFIGS[4]
+    B, Hq, Hkv, L, d, g, w = cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.g, cfg.w
+    G = Hq // Hkv
+    say(f"backward full-size {cfg.name}: generating inputs")
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    dO = cca_inputs.to_storage(cca_inputs.normal_f32(7301, (B, Hq, L, d), 1.0), "bf16")
+    qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), dO.to(DEV)
+    say("  pool, forward with statistics, backward on GPU")
+    m = L // g
+    ck = torch.empty((B, Hkv, m, d), dtype=q.dtype, device=DEV)
+    cv = torch.empty_like(ck)
+    out = torch.empty_like(qd)
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=DEV)
+    cca.cca_pool_core(qd, kd, vd, ck, cv, g)
+    cca.cca_attn_prefill_train(qd, kd, vd, ck, cv, out, lse, g, w)
+    dq = torch.empty((B, Hq, L, d), dtype=torch.float32, device=DEV)
+    dk = torch.empty((B, Hkv, L, d), dtype=torch.float32, device=DEV)
+    dv = torch.empty_like(dk)
+    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g), dtype=torch.uint8, device=DEV)
+    cca.cca_attn_backward(qd, kd, vd, ck, cv, out, lse, gd, dq, dk, dv, ws, g, w)
+    torch.cuda.synchronize()
+    r0 = L - w - 3 * g
+    deep = [t for t in (w + 5, L // 2 + 1, L // 2 + 2 * g + 7) if t % g != g - 1]
+    rows = deep + list(range(r0, L))
+    pos = [r0, r0 + g - 1, r0 + 2 * g + 3, L - w - 1, L - w, L - 700, L - g, L - 2, L - 1]
+    hk = 0
+    heads = slice(hk * G, hk * G + G)
+    dq_gpu = dq[:, heads, rows].double().cpu().numpy()
+    dk_gpu = dk[:, hk : hk + 1, pos].double().cpu().numpy()
+    dv_gpu = dv[:, hk : hk + 1, pos].double().cpu().numpy()
+    del qd, kd, vd, gd, out, dq, dk, dv, ws
+    say(f"  oracle: kv head {hk}, {len(rows)} rows, {len(pos)} key positions")
+    Qh, Kh, Vh, Gh = f32np(q[:, heads]), f32np(k[:, hk : hk + 1]), f32np(v[:, hk : hk + 1]), f32np(dO[:, heads])
+    CK, CV, _ = orc.pool_core(Qh, Kh, Vh, g)
+    dQr, dK, dV, dCK, dCV = bwd.attn_backward_rows(Qh, Kh, Vh, CK, CV, g, w, Gh, rows)
+    # pooling share of the last groups (those of every row from r0 on): the
+    # groups are independent, so pool_backward runs on the slice from group j0
+    j0 = r0 // g
+    pQ, pK, pV = bwd.pool_backward(Qh[:, :, j0 * g :], Kh[:, :, j0 * g :], Vh[:, :, j0 * g :], g,
+                                   dCK[:, :, j0:], dCV[:, :, j0:], "softmax")
+    dq_ref = dQr.copy()
+    for i, t in enumerate(rows):
+        if t >= j0 * g:
+            dq_ref[:, :, i] += pQ[:, :, t - j0 * g]
+    dk_ref = dK[:, :, pos] + pK[:, :, [p - j0 * g for p in pos]]
+    dv_ref = dV[:, :, pos] + pV[:, :, [p - j0 * g for p in pos]]
+    for name, x, y in (("dq", dq_gpu, dq_ref), ("dk", dk_gpu, dk_ref), ("dv", dv_gpu, dv_ref)):
+        e = float(np.abs(x - y).max()) / max(1.0, float(np.abs(y).max()))
+        say(f"  {name} max err / scale {e:.3e} (scale {max(1.0, float(np.abs(y).max())):.2f})")
+        assert e <= TOL["bf16"], name

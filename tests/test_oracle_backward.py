@@ -113,7 +113,38 @@ def pin_row_lse(b):
     return fails
 
 
-PINS = [pin_finite_differences, pin_reduces_to_causal_attention, pin_row_lse]
+def pin_rows_form(b):
+    """The row-restricted form equals the per-head loop: over all rows every
+    output, over a subset the dQ rows (and the contributions of those rows,
+    against the loop run on inputs whose other rows' upstream gradient is 0)."""
+    fails = []
+    for ci, (B, Hq, Hkv, L, d, g, w) in enumerate([(1, 4, 2, 37, 8, 3, 7), (2, 2, 2, 29, 4, 4, 5),
+                                                   (1, 3, 1, 20, 4, 1, 2)]):
+        Q, K, V = _rand(500 + ci, (B, Hq, L, d)), _rand(510 + ci, (B, Hkv, L, d)), _rand(520 + ci, (B, Hkv, L, d))
+        dO = _rand(530 + ci, (B, Hq, L, d))
+        CK, CV, _ = orc.pool_core(Q, K, V, g)
+        full = b.attn_backward(Q, K, V, CK, CV, g, w, dO)
+        got = b.attn_backward_rows(Q, K, V, CK, CV, g, w, dO, range(L))
+        for name, x, y in zip(("dQ", "dK", "dV", "dCK", "dCV"), got, full):
+            e = _close(x, y, 1e-12)
+            if e:
+                fails.append(f"case {ci} all rows {name}: {e}")
+        rows = [t for t in range(L) if t % 3 != 1]
+        dO_sub = dO.copy()
+        dO_sub[:, :, [t for t in range(L) if t % 3 == 1]] = 0.0
+        sub = b.attn_backward(Q, K, V, CK, CV, g, w, dO_sub)
+        got = b.attn_backward_rows(Q, K, V, CK, CV, g, w, dO, rows)
+        e = _close(got[0], full[0][:, :, rows], 1e-12)
+        if e:
+            fails.append(f"case {ci} row subset dQ: {e}")
+        for name, x, y in zip(("dK", "dV", "dCK", "dCV"), got[1:], sub[1:]):
+            e = _close(x, y, 1e-12)
+            if e:
+                fails.append(f"case {ci} row subset {name}: {e}")
+    return fails
+
+
+PINS = [pin_finite_differences, pin_reduces_to_causal_attention, pin_row_lse, pin_rows_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
