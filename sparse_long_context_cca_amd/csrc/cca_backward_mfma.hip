@@ -98,7 +98,9 @@ void dq_mfma_kernel(DqParams P) {
   static_assert(VBytes % 1024 == 0, "V tile is a whole number of wave loads");
   constexpr int NKI = KT::kLoads, NVI = VBytes / 1024, NL = NKI + NVI;
   constexpr int NLW = (NL + NW - 1) / NW, NLMIN = NL / NW;
-  __shared__ __attribute__((aligned(16))) char lds[3 * (KT::kBytes + VBytes)];
+  // K: a ring of four slots (a tile's K is read once more, by the dQ product
+  // deferred to the next iteration); V: a ring of three
+  __shared__ __attribute__((aligned(16))) char lds[4 * KT::kBytes + 3 * VBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uni(tid >> 6);
@@ -171,8 +173,8 @@ void dq_mfma_kernel(DqParams P) {
   auto tile_core = [&](int it) { return it < n_ct; };
   auto tile_base = [&](int it) { return it < n_ct ? it * kTileRows : r0 + (it - n_ct) * kTileRows; };
   auto kbuf = [&](int s) { return lds + s * KT::kBytes; };
-  auto vbuf = [&](int s) { return lds + 3 * KT::kBytes + s * VBytes; };
-  auto load_tile = [&](int slot, int it) {
+  auto vbuf = [&](int s) { return lds + 4 * KT::kBytes + s * VBytes; };
+  auto load_tile = [&](int kslot, int vslot, int it) {
     const bool core = tile_core(it);
     const int base = tile_base(it);
     const int lim = core ? nc_hi : P_hi + 1;
@@ -180,7 +182,7 @@ void dq_mfma_kernel(DqParams P) {
     const long off = (long)base * D;
     const u32x4 rk = buffer_desc((core ? ckbase : kbase) + off, nbytes);
     const u32x4 rv = buffer_desc((core ? cvbase : vbase) + off, nbytes);
-    const uint32_t kb = lds_addr(kbuf(slot)), vb = lds_addr(vbuf(slot));
+    const uint32_t kb = lds_addr(kbuf(kslot)), vb = lds_addr(vbuf(vslot));
 #pragma unroll
     for (int i = 0; i < NLW; ++i) {
       const int li = wave + NW * i;
@@ -204,10 +206,6 @@ void dq_mfma_kernel(DqParams P) {
     const int base = tile_base(it);
     return tile_core(it) ? base + kTileRows <= wnc_lo : (base >= wlo_hi && base + kTileRows - 1 <= w_lo);
   };
-  auto tile_seen = [&](int it) {  // does any row of the wave see a key of the tile?
-    const int base = tile_base(it);
-    return tile_core(it) ? base < wnc_hi : (base + kTileRows - 1 >= wlo_lo && base <= w_hi);
-  };
 
   f32x16 dqt[DB];
 #pragma unroll
@@ -215,69 +213,103 @@ void dq_mfma_kernel(DqParams P) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
   const float c = P.c;
+  // dQ^T += K^T . dS^T for chunk cc (16 keys) and dim block db of a tile
+  auto dq_mfma = [&](const char* kt, int cc, int db, const bf16x8& dsf) {
+    const char* p0 = kt + ktr_off + (4 * cc) * KT::kGroup + 64 * db;
+    const bf16x4 x0 = lds_read_tr16(p0);
+    const bf16x4 x1 = lds_read_tr16(p0 + 2 * KT::kGroup);
+    const bf16x8 a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf, dqt[db], 0, 0, 0);
+  };
 
-  load_tile(0, 0);
-  load_tile(1, 1);
+  // prologue: tiles 0 and 1; K slot 3 (read as "tile -1" with dS = 0) cleared
+  load_tile(0, 0, 0);
+  load_tile(1, 1, 1);
+  for (int i = tid; i < KT::kBytes / 16; i += kThreads)
+    *reinterpret_cast<u32x4*>(kbuf(3) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NLMIN) : "memory");
-  int slot = 0;
+  // dS of the previous tile (zeros before the first), bf16 B operands
+  bf16x8 dsb[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dsb[cc][e] = static_cast<__bf16>(0.0f);
+  // Iteration it: K(it) in K slot it%4, V(it) in V slot it%3, K(it-1) still in
+  // K slot (it-1)%4.  It loads tile it+2 (K slot (it+2)%4, V slot (it+2)%3),
+  // computes S^T and dP^T of tile it, then runs the dQ product of tile it-1
+  // interleaved with tile it's P and dS (the forward's P.V / exponential
+  // interleave): chunk cc of dsb is consumed by the product just before tile
+  // it's chunk cc overwrites it.
+  int kslot = 0, vslot = 0;
   for (int it = 0; it < n_tiles; ++it) {
-    const int nslot = slot == 0 ? 2 : slot - 1;  // (it + 2) % 3
-    load_tile(nslot, it + 2);
-    if (tile_seen(it)) {
-      const char* kt = kbuf(slot);
-      const char* vt = vbuf(slot);
-      f32x16 sx[2], dpx[2];
+    const int kprev = (kslot + 3) & 3;
+    load_tile((kslot + 2) & 3, vslot == 0 ? 2 : vslot - 1, it + 2);
+    const char* kt = kbuf(kslot);
+    const char* vt = vbuf(vslot);
+    const char* kt_prev = kbuf(kprev);
+    f32x16 sx[2], dpx[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sx[kb][r] = dpx[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sx[kb][r] = dpx[kb][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + krow_off + kb * 8 * KT::kGroup + 32 * ks);
-          sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sx[kb], 0, 0, 0);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + vrow_off + kb * 32 * VRow + 32 * ks);
-          dpx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gf[ks], dpx[kb], 0, 0, 0);
-        }
-      // P and dS of this lane's row; key kk = 32kb + 8(r/4) + 4hh + r%4
-      const bool full = tile_full(it);
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + krow_off + kb * 8 * KT::kGroup + 32 * ks);
+        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sx[kb], 0, 0, 0);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + vrow_off + kb * 32 * VRow + 32 * ks);
+        dpx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gf[ks], dpx[kb], 0, 0, 0);
+      }
+    if (!tile_full(it)) {
+      // key kk = 32kb + 8(r/4) + 4hh + r%4 of the tile is visible to this
+      // lane's row iff lo_rel <= kk <= hi_rel; hidden keys get P = 0
+      asm volatile("" ::: "memory");  // keeps this a real (scalar) branch
       const int base = tile_base(it);
       const bool core = tile_core(it);
       const int lo_rel = core ? 0 : my_lo - base;
       const int hi_rel = core ? my_nc - 1 - base : t - base;
       const unsigned span = (unsigned)(hi_rel - lo_rel);
-      bf16x8 dsb[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float ds2[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const int kk = 32 * kb + 8 * ((r + x) >> 2) + 4 * hh + ((r + x) & 3);
-            const bool vis = full || (hi_rel >= lo_rel && (unsigned)(kk - lo_rel) <= span);
-            const float p = __builtin_amdgcn_exp2f(fmaf(sx[kb][r + x], c, -lse2));
-            ds2[x] = vis ? p * (dpx[kb][r + x] - Dt) : 0.f;
-          }
-          const int cc = 2 * kb + (r >> 3), e = r & 7;
-          dsb[cc][e] = static_cast<__bf16>(ds2[0]);
-          dsb[cc][e + 1] = static_cast<__bf16>(ds2[1]);
-        }
-      // dQ^T += K^T . dS^T
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const char* p0 = kt + ktr_off + (4 * cc) * KT::kGroup + 64 * db;
-          const bf16x4 x0 = lds_read_tr16(p0);
-          const bf16x4 x1 = lds_read_tr16(p0 + 2 * KT::kGroup);
-          const bf16x8 a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsb[cc], dqt[db], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const bool vis = hi_rel >= lo_rel && (unsigned)(kk - lo_rel) <= span;
+          sx[kb][r] = vis ? sx[kb][r] : -INFINITY;
         }
     }
-    slot = slot == 2 ? 0 : slot + 1;
+    // dQ of tile it-1 interleaved with P = exp2(S c - lse2), dS = P (dP - D)
+    // of tile it: after each MFMA come the scores it can hide
+    constexpr int NDQ = 4 * DB;     // dQ MFMAs per tile
+    constexpr int PPM = 32 / NDQ;   // scores per MFMA slot
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      bf16x8 dnew;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dq_mfma(kt_prev, cc, db, dsb[cc]);
+#pragma unroll
+        for (int e = db * PPM; e < db * PPM + PPM; ++e) {
+          const int r = (cc & 1) * 8 + e;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r], c, -lse2));
+          dnew[e] = static_cast<__bf16>(p * (dpx[cc >> 1][r] - Dt));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      dsb[cc] = dnew;
+    }
+    kslot = (kslot + 1) & 3;
+    vslot = vslot == 2 ? 0 : vslot + 1;
     sync_stage();
+  }
+  // dQ of the last tile (K slot (n_tiles-1)%4)
+  {
+    const char* kt_last = kbuf((kslot + 3) & 3);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) dq_mfma(kt_last, cc, db, dsb[cc]);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
