@@ -349,11 +349,12 @@ struct DkvParams {
 };
 
 // A workgroup of 8 waves owns 128 keys.  Waves 2p and 2p+1 share keys
-// 32p .. 32p+31: per 64-row tile each computes S and dP for one half of the
-// rows, both publish P and dS in LDS, and each accumulates dV^T and dK^T
-// over all 64 rows for one half of the head dims.  (One wave per key block
-// would need some 330 registers; split this way a wave fits in 256, two per
-// SIMD.)
+// 32p .. 32p+31 and split each 64-row tile: each computes S, dP, P and dS for
+// its 32 rows and accumulates dV^T and dK^T over them for all head dims; the
+// two partial sums meet once, through LDS, when the unit is done.  The K
+// fragments of the wave's keys stay in registers, the V fragments sit in LDS
+// (registers for both would take a wave past 256, and one wave per SIMD
+// left the compiler shuttling accumulators between register files).
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkv_mfma_kernel(DkvParams P) {
@@ -364,10 +365,11 @@ void dkv_mfma_kernel(DkvParams P) {
   static_assert(RT::kBytes - RT::kBytesUsed >= 512, "room for the row statistics");
   constexpr int QTailLanes = (RT::kBytesUsed - (RT::kLoads - 1) * 1024) / 16;  // live lanes of Q's last load
   constexpr int SlotBytes = 2 * RT::kBytes;
-  constexpr int XBytes = NW * 4 * 1024;  // per wave: P and dS fragments of two k-steps
+  constexpr int VFBytes = (NW / 2) * KS * 1024;  // per wave pair: V fragments [ks][lane]
+  static_assert((NW / 2) * 2 * DB * 4 * 1024 <= 3 * SlotBytes + VFBytes, "partial sums fit in LDS");
   constexpr int NL = 2 * RT::kLoads + 1;
   constexpr int NLW = (NL + NW - 1) / NW, NLMIN = NL / NW;
-  __shared__ __attribute__((aligned(16))) char lds[3 * SlotBytes + XBytes];
+  __shared__ __attribute__((aligned(16))) char lds[3 * SlotBytes + VFBytes];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uni(tid >> 6);
@@ -430,19 +432,22 @@ void dkv_mfma_kernel(DkvParams P) {
   const long kvrow = (long)kvp;
   const uint16_t* kb_ = core ? P.ck + kvrow * P.m_cap * D : P.k + kvrow * L * D;
   const uint16_t* vb_ = core ? P.cv + kvrow * P.m_cap * D : P.v + kvrow * L * D;
-  bf16x8 kf[KS], vf[KS];
+  char* vfrag = lds + 3 * SlotBytes + pair * KS * 1024 + 16 * lane;  // V fragment ks at + 1024 ks
+  bf16x8 kf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 vx;
     if (key_ok) {
       kf[ks] = *reinterpret_cast<const bf16x8*>(kb_ + (long)key * D + 16 * ks + 8 * hh);
-      vf[ks] = *reinterpret_cast<const bf16x8*>(vb_ + (long)key * D + 16 * ks + 8 * hh);
+      vx = *reinterpret_cast<const bf16x8*>(vb_ + (long)key * D + 16 * ks + 8 * hh);
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kf[ks][e] = vf[ks][e] = static_cast<__bf16>(0.0f);
+      for (int e = 0; e < 8; ++e) kf[ks][e] = vx[e] = static_cast<__bf16>(0.0f);
     }
+    if (half == 0) *reinterpret_cast<bf16x8*>(vfrag + 1024 * ks) = vx;
   }
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]), "v"(vf[ks]));
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]));
 
   // ---- tile loaders: load index li < RT::kLoads fills Q, then dO, then the statistics
   int soff[NLW];
@@ -456,7 +461,6 @@ void dkv_mfma_kernel(DkvParams P) {
   auto qbuf = [&](int s) { return lds + s * SlotBytes; };
   auto gbuf = [&](int s) { return lds + s * SlotBytes + RT::kBytes; };
   auto sbuf = [&](int s) { return lds + s * SlotBytes + RT::kBytesUsed; };
-  char* xbuf = lds + 3 * SlotBytes;
   auto load_tile = [&](int slot, int it) {
     const int hg = it / n_rt, tile = it % n_rt;
     const int t0 = t_lo + tile * kTileRows;
@@ -494,14 +498,11 @@ void dkv_mfma_kernel(DkvParams P) {
   // row 16cc + 8x + 4hh + s/4, dims 32db + 16((lane/16)%2) + 4(s%4) .. +3
   const int rrow_off = RT::row_off(32 * half + i32) + 16 * hh;
   const int s16 = lane & 15;
-  const int rtr_off = hh * RT::kGroup + (s16 >> 2) * RT::kRow + 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3)) +
-                      64 * DBH * half;
-  char* xmine = xbuf + wave * 4096 + 16 * lane;           // [frag][lane] of this wave
-  const char* xpair = xbuf + (2 * pair) * 4096 + 16 * lane;  // the pair's first wave
+  const int rtr_off = hh * RT::kGroup + (s16 >> 2) * RT::kRow + 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
 
-  f32x16 dkt[DBH], dvt[DBH];
+  f32x16 dkt[DB], dvt[DB];
 #pragma unroll
-  for (int db = 0; db < DBH; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
   const float c = P.c;
@@ -528,14 +529,15 @@ void dkv_mfma_kernel(DkvParams P) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + rrow_off + 32 * ks);
       sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sx, 0, 0, 0);
       const bf16x8 ag = *reinterpret_cast<const bf16x8*>(gt + rrow_off + 32 * ks);
-      dpx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf[ks], dpx, 0, 0, 0);
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vfrag + 1024 * ks);
+      dpx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf, dpx, 0, 0, 0);
     }
-    // P and dS (bf16 fragments, k-steps 2 half and 2 half + 1) into LDS
+    // P and dS (bf16 fragments of k-steps 2 half and 2 half + 1)
     const bool full = wave_keys_ok && tw >= lo_max && tw + 31 <= hi_min;
-    auto publish = [&](auto mask_tag) {
+    bf16x8 pb[2], dsb[2];
+    auto probs = [&](auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const unsigned span = (unsigned)(hi - lo);
-      bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int rr = 32 * half + 8 * q4 + 4 * hh;  // tile row of this lane's first of 4
@@ -555,30 +557,22 @@ void dkv_mfma_kernel(DkvParams P) {
           dsb[q4 >> 1][4 * (q4 & 1) + x] = static_cast<__bf16>(p * (dpx[r] - dd[x]));
         }
       }
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        *reinterpret_cast<bf16x8*>(xmine + h2 * 1024) = pb[h2];
-        *reinterpret_cast<bf16x8*>(xmine + (2 + h2) * 1024) = dsb[h2];
-      }
     };
-    if (full) publish(std::false_type{});
-    else publish(std::true_type{});
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // dV^T += dO^T . P and dK^T += Q^T . dS over the 64 rows, this wave's dims
+    if (full) probs(std::false_type{});
+    else probs(std::true_type{});
+    // dV^T += dO^T . P and dK^T += Q^T . dS over this wave's 32 rows, all dims
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const char* xf = xpair + (cc >> 1) * 4096 + (cc & 1) * 1024;
-      const bf16x8 pbf = *reinterpret_cast<const bf16x8*>(xf);
-      const bf16x8 dsf = *reinterpret_cast<const bf16x8*>(xf + 2048);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int cc = 2 * half + h2;
 #pragma unroll
-      for (int db = 0; db < DBH; ++db) {
+      for (int db = 0; db < DB; ++db) {
         const int o = rtr_off + (4 * cc) * RT::kGroup + 64 * db;
         const bf16x4 g0 = lds_read_tr16(gt + o), g1 = lds_read_tr16(gt + o + 2 * RT::kGroup);
         const bf16x8 ag = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pbf, dvt[db], 0, 0, 0);
+        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pb[h2], dvt[db], 0, 0, 0);
         const bf16x4 q0 = lds_read_tr16(qt + o), q1 = lds_read_tr16(qt + o + 2 * RT::kGroup);
         const bf16x8 aq = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsf, dkt[db], 0, 0, 0);
+        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[h2], dkt[db], 0, 0, 0);
       }
     }
     slot = slot == 2 ? 0 : slot + 1;
@@ -586,16 +580,45 @@ void dkv_mfma_kernel(DkvParams P) {
     sync_stage();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the pair's two partial sums meet in LDS (the ring is idle now): the
+  // second wave writes its accumulators, the first adds them and stores
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  float4* part = reinterpret_cast<float4*>(lds) + (size_t)pair * (2 * DB * 4 * 64) + lane;
+  if (half == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        part[((0 * DB + db) * 4 + q4) * 64] = make_float4(dkt[db][4 * q4], dkt[db][4 * q4 + 1], dkt[db][4 * q4 + 2], dkt[db][4 * q4 + 3]);
+        part[((1 * DB + db) * 4 + q4) * 64] = make_float4(dvt[db][4 * q4], dvt[db][4 * q4 + 1], dvt[db][4 * q4 + 2], dvt[db][4 * q4 + 3]);
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (half == 1 || !key_ok) return;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 a = part[((0 * DB + db) * 4 + q4) * 64];
+      const float4 v = part[((1 * DB + db) * 4 + q4) * 64];
+      dkt[db][4 * q4] += a.x;
+      dkt[db][4 * q4 + 1] += a.y;
+      dkt[db][4 * q4 + 2] += a.z;
+      dkt[db][4 * q4 + 3] += a.w;
+      dvt[db][4 * q4] += v.x;
+      dvt[db][4 * q4 + 1] += v.y;
+      dvt[db][4 * q4 + 2] += v.z;
+      dvt[db][4 * q4 + 3] += v.w;
+    }
 
-  // lane holds dims 32(DBH half + db) + 8(r/4) + 4hh + r%4 of its key
-  if (!key_ok) return;
+  // lane holds dims 32db + 8(r/4) + 4hh + r%4 of its key
   if (!core) {
     const long orow = ((long)kvp * L + key) * D;
 #pragma unroll
-    for (int db = 0; db < DBH; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * (DBH * half + db) + 8 * q4 + 4 * hh;
+        const int d0 = 32 * db + 8 * q4 + 4 * hh;
         *reinterpret_cast<float4*>(P.dk + orow + d0) =
             make_float4(dkt[db][4 * q4] * P.scale, dkt[db][4 * q4 + 1] * P.scale,
                         dkt[db][4 * q4 + 2] * P.scale, dkt[db][4 * q4 + 3] * P.scale);
@@ -605,10 +628,10 @@ void dkv_mfma_kernel(DkvParams P) {
   } else {
     const long orow = ((long)kvp * P.m + key) * D;
 #pragma unroll
-    for (int db = 0; db < DBH; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int d = 32 * (DBH * half + db) + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int d = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
         atomicAdd(P.dck + orow + d, dkt[db][r] * P.scale);
         atomicAdd(P.dcv + orow + d, dvt[db][r]);
       }
