@@ -174,7 +174,8 @@ cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, c
 
 /*
  * cca_attn_backward_workspace_bytes - device workspace cca_attn_backward needs
- *   (fp32 row statistics [B,Hq,L] and core gradients 2 x [B,Hkv,L/g,d]).
+ *   (two fp32 row statistics per row, [B,Hq,L,2], and the core gradients
+ *   2 x [B,Hkv,L/g,d] fp32); 0 for sizes below 1.
  */
 size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g);
 

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* __restri
   if (valid && part == 0) stats[row] = make_float2(lse[row] * kLog2e, acc);
 }
 
+// A wave-uniform value held in a scalar register.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // ------------------------------------------------------------------ 2. dQ
