@@ -82,6 +82,11 @@ BWD_CASES = [
     ("bf16", 2, 16, 2, 333, 128, 8, 50, cca.CCA_POOL_MAX),
     ("bf16", 1, 4, 1, 129, 128, 1, 16, cca.CCA_POOL_SOFTMAX),
     ("bf16", 1, 2, 1, 90, 64, 16, 200, cca.CCA_POOL_SOFTMAX_HEADS),  # w >= L: no core visible
+    ("bf16", 1, 16, 1, 100, 128, 16, 32, cca.CCA_POOL_SOFTMAX),  # G = 16: 8 heads per dQ workgroup
+    ("bf16", 3, 6, 3, 70, 64, 5, 9, cca.CCA_POOL_MEAN),          # B * Hkv = 9: no XCD mapping
+    ("bf16", 2, 16, 8, 200, 128, 16, 64, cca.CCA_POOL_SOFTMAX),  # B * Hkv = 16: 2 kv heads per XCD
+    ("bf16", 1, 2, 1, 1, 128, 16, 4, cca.CCA_POOL_SOFTMAX),      # L = 1
+    ("bf16", 1, 4, 2, 40, 128, 64, 8, cca.CCA_POOL_MAX),         # g > L: no core at all
 ]
 
 
