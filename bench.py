@@ -301,7 +301,7 @@ def main():
                          "calibration reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no sharding or collectives); "
+        print("bench.py: the library runs on one GPU only (it has no sharding or collectives); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
