@@ -41,7 +41,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTileRows = 64;    // keys per tile (dQ), rows per tile (dK dV)
 constexpr int kKeysPerUnit = 128;  // keys per dK dV workgroup (4 wave pairs x 32)
-constexpr int kCoreSplit = 4096;   // rows per core unit (absolute, aligned splits)
+constexpr int kCoreSplit = 8192;   // rows per core unit (absolute, aligned splits)
 
 // ------------------------------------------------------------- 1. statistics
 

@@ -76,8 +76,8 @@ BWD_CASES = [
     ("f32", 1, 2, 1, 150, 64, 1, 8, cca.CCA_POOL_SOFTMAX),     # g = 1: every token its own core
     ("f32", 1, 2, 2, 100, 64, 16, 200, cca.CCA_POOL_SOFTMAX),  # w >= L: no core visible
     # bf16 inputs run the matrix-core kernels: several 128-key core blocks, core
-    # rows split at 4096-row boundaries, ragged tiles, d = 64, G = 8, g = 1
-    ("bf16", 1, 8, 2, 5000, 128, 16, 256, cca.CCA_POOL_SOFTMAX),
+    # rows split at 8192-row boundaries, ragged tiles, d = 64, G = 8, g = 1
+    ("bf16", 1, 8, 2, 9000, 128, 16, 256, cca.CCA_POOL_SOFTMAX),
     ("bf16", 1, 2, 2, 700, 64, 4, 100, cca.CCA_POOL_MEAN),
     ("bf16", 2, 16, 2, 333, 128, 8, 50, cca.CCA_POOL_MAX),
     ("bf16", 1, 4, 1, 129, 128, 1, 16, cca.CCA_POOL_SOFTMAX),
