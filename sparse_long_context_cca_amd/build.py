@@ -25,11 +25,18 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Wall", "-Wno-unused-function"]
+# Per-source flags.  The prefill kernel's main loop is scheduled with the
+# backend's iterative ILP strategy: measured in one process on one MI355X it
+# is about 2 % faster on the GQA 128K prefill and 3 % on the MHA 32K one (the
+# same strategy slows the backward kernels, which keep the default).
+SOURCE_FLAGS = {
+    "cca_prefill_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
