@@ -6,7 +6,9 @@ A step is one pass of the prefill hot path over the LLaMA-3.1-8B GQA workload
 bf16): cca_pool_core then cca_attn_prefill, inputs already resident in HBM.
 The backward pass over the same workload (cca_attn_backward) and the decode
 workload (batch 8, 32/8 heads, 65536 cached tokens, 256 single-token steps) are
-timed in the same run and reported under "backward" and "decode".
+timed in the same run and reported under "backward" and "decode"; a large bf16
+GEMM and a device-to-device copy give measured ceilings ("reference_rates")
+next to the spec peaks.
 
 Prints ONE JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
 --warmup W, --no-cpu (skip the CPU-oracle baseline), --no-decode, --no-backward.
@@ -201,6 +203,35 @@ def bench_backward(cca, cfg, qd, kd, vd, steps=2, warmup=1):
             "achieved_TFLOP_per_s": tflops, "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
             "frac": tflops / PEAK_BF16_TFLOPS, "executed_mfma_flops": 14.0 * d * pairs,
             "note": "bf16 matrix-core kernels (fp32 accumulate); gradients fp32"}
+
+
+def reference_rates(dev="cuda:0", n=16384, copy_bytes=1 << 30, reps=10):
+    """Measured ceilings on this GPU next to the spec peaks: a large dense bf16
+    GEMM through torch (hipBLASLt) and a device-to-device copy, each timed with
+    events over `reps` runs after one warm-up."""
+    a = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    c = a @ b
+    src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e[1].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e[2].record()
+    torch.cuda.synchronize()
+    gemm_ms = e[0].elapsed_time(e[1]) / reps
+    copy_ms = e[1].elapsed_time(e[2]) / reps
+    del a, b, c, src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_TFLOP_per_s": 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12, "gemm_shape": f"{n}x{n}x{n}",
+            "d2d_copy_GB_per_s": 2.0 * copy_bytes / (copy_ms * 1e-3) / 1e9,
+            "copy_bytes": copy_bytes, "copy_note": "read + write bytes per copy"}
 
 
 def bench_decode(cca, cfg, steps_timed=True):
@@ -399,6 +430,16 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] decode", file=sys.stderr, flush=True)
         result["decode"] = bench_decode(cca, cca_inputs.CONFIGS[5])
+    # measured ceilings: the prefill against a large bf16 GEMM, pooling and
+    # decode against a device-to-device copy
+    print("[bench] reference rates", file=sys.stderr, flush=True)
+    ref = reference_rates()
+    result["reference_rates"] = ref
+    result["roofline"]["frac_of_measured_gemm"] = tflops / ref["bf16_gemm_TFLOP_per_s"]
+    if result["pool"]["GB_per_s"]:
+        result["pool"]["frac_of_measured_copy"] = result["pool"]["GB_per_s"] / ref["d2d_copy_GB_per_s"]
+    if "decode" in result:
+        result["decode"]["frac_of_measured_copy"] = result["decode"]["GB_per_s"] / ref["d2d_copy_GB_per_s"]
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_oracle_baseline(cfg, q, k, v)
