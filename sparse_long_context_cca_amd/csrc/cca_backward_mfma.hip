@@ -14,17 +14,21 @@
 //   1. row_stats_kernel  per row {lse * log2(e), D_t}
 //   2. dq_mfma_kernel    row-parallel, the forward's work decomposition: per
 //                        64-key tile S^T = K.Q^T and dP^T = V.dO^T (K, V rows
-//                        from LDS, Q and dO fragments in registers), then
-//                        dQ^T += K^T.dS^T with K^T through transposing reads
+//                        from LDS, Q and dO fragments in registers), and
+//                        dQ^T += K^T.dS^T with K^T through transposing reads;
+//                        the dQ product of tile i-1 is interleaved with tile
+//                        i's exponentials, as in the forward
 //   3. dkv_mfma_kernel   key-parallel: a workgroup owns 128 keys (raw
-//                        positions, or cores) of one kv head, each pair of
-//                        waves 32 of them with their K and V fragments in
-//                        registers, and walks the rows that see them for every
-//                        query head of the group: S = Q.K^T, dP = dO.V^T (Q,
-//                        dO rows from LDS), dV^T += dO^T.P and dK^T += Q^T.dS
-//                        (dO^T, Q^T through transposing reads).  Raw keys get
-//                        plain stores; core rows are split over workgroups and
-//                        meet by atomic adds in an fp32 workspace.
+//                        positions, or cores) of one kv head and walks the
+//                        rows that see them for every query head of the
+//                        group.  A pair of waves shares 32 keys (K fragments
+//                        in registers, V fragments in LDS) and splits each
+//                        tile's rows: S = Q.K^T, dP = dO.V^T (Q, dO rows from
+//                        LDS), dV^T += dO^T.P and dK^T += Q^T.dS (dO^T, Q^T
+//                        through transposing reads) for all head dims; the
+//                        pair's partial sums meet in LDS at the end.  Raw keys
+//                        get plain stores; core rows are split over workgroups
+//                        and meet by atomic adds in an fp32 workspace.
 // The pooling share of the gradients is added afterwards by the pooling
 // backward of cca_backward.hip.
 #include <algorithm>
