@@ -24,7 +24,10 @@
 //   S^T (64 keys x 32 rows) = K_tile . Q^T with v_mfma_f32_32x32x16_bf16
 //   (A = K rows from LDS, B = the wave's Q fragments, held in registers);
 //   each lane then holds 32 scores of one query row, so the row max needs one
-//   exchange with lane l^32, and the row sum is kept per lane until the end.
+//   exchange with lane l^32.  The row sum of the rounded probabilities is
+//   taken on the matrix cores too: one 16x16x32 MFMA per P chunk whose A
+//   operand selects, for output rows 0 and 1, the lanes that hold query rows
+//   0..15 and 16..31 (the sum does not depend on the key order).
 //   P (bf16) is used in place as the B operand of O^T += V^T . P^T; the V^T
 //   operand comes from a row-major V tile through transposing LDS reads that
 //   follow the key order of the score layout.  The P.V product of tile i-1
@@ -63,14 +66,10 @@ struct PrefillParams {
 // Lanes l and l^32 hold the two halves of one query row's scores.  One
 // v_permlane32_swap of a register with itself leaves {x[l], x[l^32]} in the
 // two results (in an order that differs between the lane halves), so the
-// pair max and pair sum below are symmetric in them.
+// pair max below is symmetric in them.
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Two waves per SIMD (the accumulators stay in arch VGPRs, 256 per wave) so
@@ -260,10 +259,30 @@ void prefill_mfma_kernel(PrefillParams P) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY;
+  // Row sums: a 16x16x32 MFMA reads its B operand as B[k = 8(l/16) + e][l%16]
+  // for lane l, so with A[0][k] = 1 on k in [0,8) u [16,24) (lanes 0 and 32
+  // of the A operand) and A[1][k] = 1 on [8,16) u [24,32) (lanes 17 and 49),
+  // C[0][c] adds lanes c and c+32 of a P chunk (query row c) and C[1][c] lanes
+  // c+16 and c+48 (query row c+16).  Lane c < 16 holds C[0][c] and C[1][c]
+  // in lsum[0] and lsum[1]; the other rows of C stay zero.
+  f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
+  bf16x8 sel;
+  {
+    const bool on = lane == 0 || lane == 32 || lane == 17 || lane == 49;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[e] = static_cast<__bf16>(on ? 1.0f : 0.0f);
+  }
+  auto row_sum_mfma = [&](const bf16x8& p) { lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p, lsum, 0, 0, 0); };
+  // rescale the row sums by their rows' factors (lane c < 16 needs those of
+  // rows c and c+16, held by lanes c and c+16)
+  auto rescale_sums = [&](float a) {
+    const float a_hi = __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & 15) + 16) * 4, __float_as_int(a)));
+    lsum[0] *= a;
+    lsum[1] *= a_hi;
+  };
   const float c = P.c;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   // End of a pipeline stage: this wave's loads of the previous stage (K(it+1),
   // V(it)) have landed in LDS, then the workgroup meets.  Loads finish in
@@ -311,6 +330,7 @@ void prefill_mfma_kernel(PrefillParams P) {
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
+      rescale_sums(alpha_pending);
     }
     const char* kt = kbuf(kslot);
     const char* vt_prev = vbuf(prev);
@@ -360,11 +380,10 @@ void prefill_mfma_kernel(PrefillParams P) {
     const float ex = __builtin_amdgcn_exp2f((m - mnew) * c);  // NaN while both are -inf; unused then
     const float alpha = grow ? ex : 1.0f;
     m = grow ? mnew : m;
-    l *= alpha;
     const float mc = (m == -INFINITY ? 0.f : m) * c;
     // P.V of tile it-1 interleaved by hand with tile it's exponentials: after
     // each MFMA (32 cycles on the matrix core) come the probabilities it can
-    // hide (2 fma, 2 exp, 1 convert, 1 dot2 per pair).  sched_barrier freezes
+    // hide (2 fma, 2 exp, 1 convert per pair).  sched_barrier freezes
     // that order; V^T fragments are read two MFMAs ahead through a ring of 3.
     static_assert(DB == 2 || DB == 4, "head dim 64 or 128");
     constexpr int PPM = 8 / DB;  // probabilities per MFMA slot
@@ -389,13 +408,12 @@ void prefill_mfma_kernel(PrefillParams P) {
           bf16x2 pk;
           pk[0] = static_cast<__bf16>(p0);
           pk[1] = static_cast<__bf16>(p1);
-          // row sum of the rounded probabilities actually fed to P.V
-          l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l, false);
           pnew[e] = pk[0];
           pnew[e + 1] = pk[1];
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      row_sum_mfma(pr[cc]);  // tile it-1's chunk cc, then replaced by tile it's
       pr[cc] = pnew;
     }
     grow_pending = __builtin_amdgcn_ballot_w64(grow) != 0;
@@ -412,6 +430,7 @@ void prefill_mfma_kernel(PrefillParams P) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
+    rescale_sums(alpha_pending);
   }
   {
     const char* vt = vbuf(kslot == 0 ? 2 : kslot - 1);  // V(n_tiles - 1)
@@ -420,10 +439,15 @@ void prefill_mfma_kernel(PrefillParams P) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag_at(vt, cc, db), pr[cc], o[db], 0, 0, 0);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) row_sum_mfma(pr[cc]);
   }
 
   // ---- normalise and store: lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
-  const float ltot = pair_sum(l);
+  // row j's sum: lane j%16 holds it, in lsum[0] for j < 16 and lsum[1] above
+  const float l_lo = __int_as_float(__builtin_amdgcn_ds_bpermute((j & 15) * 4, __float_as_int(lsum[0])));
+  const float l_hi = __int_as_float(__builtin_amdgcn_ds_bpermute((j & 15) * 4, __float_as_int(lsum[1])));
+  const float ltot = j < 16 ? l_lo : l_hi;
   const float inv = 1.0f / ltot;
   if (t_raw < Le) {
     const long orow = (((long)b * P.Hq + h) * P.Lq + (t_raw - qs)) * D;
