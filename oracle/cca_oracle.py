@@ -228,6 +228,40 @@ def attn_rows_q(qrows, K, V, CK, CV, g: int, w: int, ts):
     return out
 
 
+def attn_rows_masked(Q, K, V, CK, CV, g: int, w: int, t0: int, t1: int):
+    """Rows t0..t1-1 (consecutive) of ``attn_rows`` evaluated together.
+
+    The same definition written with a mask, for checking many rows at once:
+    every row of the range is scored against the cores 0..n_core(t1-1)-1 and
+    the raw positions win_lo(t0)..t1-1 (the union of the rows' visible sets),
+    the scores of keys outside the row's own sets (core j >= n_core(t); raw
+    position p < win_lo(t) or p > t) are set to -inf, and ONE softmax over
+    [cores ; raw] weights the matching values.  Masked keys get probability
+    exactly zero, so each row equals ``attn_rows`` for that row.
+    Returns O [B,Hq,t1-t0,d] in fp64.
+    """
+    B, Hq, _, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    ts = np.arange(t0, t1)
+    nc = np.array([n_core(int(t), g, w) for t in ts])
+    lo = np.array([win_lo(int(t), w) for t in ts])
+    NC, LO = int(nc.max()), int(lo.min())
+    q = _f64(Q[:, :, t0:t1, :]).reshape(B, Hkv, G, len(ts), d)      # R-9: head h -> kv head h//G
+    ck, cv = _f64(CK[:, :, None, :NC, :]), _f64(CV[:, :, None, :NC, :])
+    kw, vw = _f64(K[:, :, None, LO:t1, :]), _f64(V[:, :, None, LO:t1, :])
+    scale = 1.0 / math.sqrt(d)
+    sc = (q @ np.swapaxes(ck, -1, -2)) * scale                      # [B,Hkv,G,n,NC]
+    sr = (q @ np.swapaxes(kw, -1, -2)) * scale                      # [B,Hkv,G,n,t1-LO]
+    core_vis = np.arange(NC)[None, :] < nc[:, None]
+    raw_pos = np.arange(LO, t1)[None, :]
+    raw_vis = (raw_pos >= lo[:, None]) & (raw_pos <= ts[:, None])
+    s = np.concatenate([np.where(core_vis, sc, -np.inf), np.where(raw_vis, sr, -np.inf)], axis=-1)
+    p = _softmax(s, axis=-1)                                          # one softmax over [cores ; window]
+    o = p[..., :NC] @ cv + p[..., NC:] @ vw
+    return o.reshape(B, Hq, len(ts), d)
+
+
 def attn_prefill(Q, K, V, CK, CV, g: int, w: int):
     """All L rows of causal prefill (see ``attn_rows``)."""
     return attn_rows(Q, K, V, CK, CV, g, w, range(Q.shape[2]))

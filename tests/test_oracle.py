@@ -401,9 +401,28 @@ def pin_pool_modes(o):
     return fails
 
 
+def pin_masked_rows_form(o):
+    """The masked multi-row form (used to check consecutive rows at full
+    size) equals the per-row form on every row, for ranges that start and end
+    anywhere: GQA, MHA, g = 1, g > w, w >= L, rows before the first core."""
+    fails = []
+    cases = [(2, 4, 2, 70, 8, 3, 5, 13), (1, 8, 2, 64, 16, 4, 16, 9), (1, 2, 2, 40, 8, 1, 7, 6),
+             (1, 3, 1, 33, 8, 40, 60, 33), (1, 4, 1, 90, 8, 5, 12, 128), (1, 2, 1, 50, 8, 6, 2, 7)]
+    for i, (B, Hq, Hkv, L, d, g, w, n) in enumerate(cases):
+        Q, K, V = _rand(900 + i, (B, Hq, L, d)), _rand(910 + i, (B, Hkv, L, d)), _rand(920 + i, (B, Hkv, L, d))
+        CK, CV, _ = o.pool_core(Q, K, V, g)
+        ref = o.attn_rows(Q, K, V, CK, CV, g, w, range(L))
+        got = np.concatenate([o.attn_rows_masked(Q, K, V, CK, CV, g, w, t0, min(L, t0 + n))
+                              for t0 in range(0, L, n)], axis=2)
+        e = _close(got, ref, 1e-12)
+        if e:
+            fails.append(f"B={B} Hq={Hq} Hkv={Hkv} L={L} g={g} w={w} rows of {n}: {e}")
+    return fails
+
+
 PINS = [pin_visibility_vs_sets, pin_pair_counts, pin_kv_cache_size, pin_pool_worked_example,
         pin_pool_invariants, pin_pool_gqa, pin_reduces_to_full_causal, pin_visible_set_one_hot,
-        pin_brute_force, pin_convex_hull, pin_decode_is_prefill_row, pin_pool_modes]
+        pin_brute_force, pin_convex_hull, pin_decode_is_prefill_row, pin_pool_modes, pin_masked_rows_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -473,8 +492,23 @@ def _rows_transposed_heads(Q, K, V, CK, CV, g, w, ts):
     return out[:, inv]
 
 
+def _masked_window_one_long(Q, K, V, CK, CV, g, w, t0, t1):
+    return _ORIG_MASKED(Q, K, V, CK, CV, g, w + 1, t0, t1)
+
+
+def _masked_rows_shifted(Q, K, V, CK, CV, g, w, t0, t1):
+    # rows of the range computed one position late (the last one early)
+    L = Q.shape[2]
+    a, b = min(t0 + 1, L - 1), min(t1 + 1, L)
+    out = _ORIG_MASKED(Q, K, V, CK, CV, g, w, a, b)
+    if out.shape[2] < t1 - t0:
+        out = np.concatenate([out, _ORIG_MASKED(Q, K, V, CK, CV, g, w, L - 1, L)], axis=2)
+    return out[:, :, : t1 - t0]
+
+
 _ORIG_POOL = orc.pool_core
 _ORIG_ROWS = orc.attn_rows
+_ORIG_MASKED = orc.attn_rows_masked
 
 FN_MUTATIONS = {
     "pooling scores not scaled by 1/sqrt(d)": ("pool_core", _pool_no_scale),
@@ -484,6 +518,8 @@ FN_MUTATIONS = {
     "per-head softmax rule averages logits": ("pool_core", _pool_heads_average_logits),
     "mean pooling divides by g-1": ("pool_core", _pool_mean_over_g_minus_1),
     "query head -> kv head map transposed": ("attn_rows", _rows_transposed_heads),
+    "masked rows: window one token long": ("attn_rows_masked", _masked_window_one_long),
+    "masked rows: rows shifted by one": ("attn_rows_masked", _masked_rows_shifted),
 }
 
 
