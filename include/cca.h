@@ -39,7 +39,8 @@
  *   - Input dtype `dt` applies to q, k, v and the core/ring caches.
  *     Supported: d in {64, 128}; dt in {CCA_F32, CCA_BF16}; out_dt in
  *     {dt, CCA_F32}.  Every buffer must hold at most 2^40 elements (offsets are
- *     64-bit).
+ *     64-bit); sequence lengths, g, w, the ring size R and m_cap are below
+ *     2^30 (positions are 32-bit).  Beyond either: CCA_ERR_UNSUPPORTED.
  *   - Rounding: accumulation is fp32; core K/V and outputs are rounded to their
  *     storage dtype once, to nearest even.  bf16 attention feeds the matrix
  *     cores bf16 operands (probabilities are rounded to bf16 before P*V).
@@ -57,7 +58,7 @@ extern "C" {
 typedef enum cca_status {
   CCA_OK = 0,
   CCA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, bad enum */
-  CCA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, dtype combination, Hq % Hkv != 0 */
+  CCA_ERR_UNSUPPORTED = 2, /* d not in {64,128}, dtype combination, Hq % Hkv != 0, size limits */
   CCA_ERR_CAPACITY = 3,    /* m_cap < L/g, ring R < max(w, g), workspace too small */
   CCA_ERR_HIP = 4          /* a HIP launch failed; see cca_last_error() */
 } cca_status;
@@ -279,10 +280,11 @@ size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int 
  *   out: [B,Hq,d] in out_dt.  workspace: device memory of at least
  *   cca_decode_workspace_bytes(...) bytes, contents need no initialisation.
  *   pos: int32 [B] device array; read, and incremented by one after the step
- *   when advance_pos != 0 (so that a step can be replayed in a loop).
- *   A sequence with t < 0 or floor((t+1)/g) > m_cap (no core slot left) gets
- *   NaN outputs and no cache writes (pos lives on the device, so this cannot
- *   be reported as a status).
+ *   when advance_pos != 0 (so that a step can be replayed in a loop; it stays
+ *   at INT32_MAX once there).
+ *   A sequence with t < 0, t = INT32_MAX or floor((t+1)/g) > m_cap (no core
+ *   slot left) gets NaN outputs and no cache writes (pos lives on the device,
+ *   so this cannot be reported as a status).
  * Errors: INVALID_ARG, UNSUPPORTED as above; CAPACITY when R < max(w, g) or
  *   the workspace is too small.
  */

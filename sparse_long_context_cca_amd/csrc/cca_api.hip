@@ -66,6 +66,16 @@ cca_status check_out_dt(const char* fn, int out_dt, int dt) {
   return CCA_OK;
 }
 
+// Sequence lengths, positions, g, w, R and m_cap stay below 2^30, so that
+// the kernels' 32-bit sums of two of them (a position plus g or w, the end of
+// a row block) cannot overflow.  Pass -1 for an extent that does not apply.
+const int kMaxExtent = (1 << 30) - 1;
+cca_status check_extents(const char* fn, int L, int g, int w, int other) {
+  if (L > kMaxExtent || g > kMaxExtent || w > kMaxExtent || other > kMaxExtent)
+    return fail(CCA_ERR_UNSUPPORTED, "%s: lengths, g, w, R and m_cap must be below 2^30", fn);
+  return CCA_OK;
+}
+
 cca_status check_sizes(const char* fn, long long a, long long b, long long c) {
   if (a > kMaxElems || b > kMaxElems || c > kMaxElems)
     return fail(CCA_ERR_UNSUPPORTED, "%s: a buffer exceeds 2^40 elements", fn);
@@ -96,6 +106,7 @@ cca_status cca_visibility_table(int L, int g, int w, int32_t* n_core, int32_t* w
   const char* fn = "cca_visibility_table";
   if (L < 1 || g < 1 || w < 1)
     return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
+  if (check_extents(fn, L, g, w, -1) != CCA_OK) return CCA_ERR_UNSUPPORTED;
   REQUIRE_PTR(n_core);
   REQUIRE_PTR(win_lo);
   if (L / g > 0) REQUIRE_PTR(group_last);
@@ -122,6 +133,8 @@ cca_status pool_core(const char* fn, const void* q, const void* k, const void* v
                      int g, cca_dtype dt, int mode, void* stream) {
   if (L < 1 || g < 1) return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d must be >= 1", fn, L, g);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_extents(fn, L, g, -1, m_cap);
   if (st != CCA_OK) return st;
   st = check_pool_mode(fn, mode, Hq, Hkv);
   if (st != CCA_OK) return st;
@@ -187,6 +200,8 @@ cca_status cca_pool_core_chunk(const void* q, const void* k, const void* v, void
   if (st != CCA_OK) return st;
   st = check_rows(fn, q_start, q_len, Lq, Lk);
   if (st != CCA_OK) return st;
+  st = check_extents(fn, Lq > Lk ? Lq : Lk, g, -1, m_cap);
+  if (st != CCA_OK) return st;
   if (mode == CCA_POOL_SOFTMAX || mode == CCA_POOL_SOFTMAX_HEADS) REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
@@ -216,6 +231,8 @@ cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, cons
   if (L < 1 || g < 1 || w < 1)
     return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_extents(fn, L, g, w, m_cap);
   if (st != CCA_OK) return st;
   st = check_out_dt(fn, out_dt, dt);
   if (st != CCA_OK) return st;
@@ -259,6 +276,8 @@ cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, c
     return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
   if (st != CCA_OK) return st;
+  st = check_extents(fn, L, g, w, m_cap);
+  if (st != CCA_OK) return st;
   st = check_out_dt(fn, out_dt, dt);
   if (st != CCA_OK) return st;
   REQUIRE_PTR(q);
@@ -299,6 +318,8 @@ cca_status cca_attn_backward(const void* q, const void* k, const void* v, const 
   if (L < 1 || g < 1 || w < 1)
     return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
+  if (st != CCA_OK) return st;
+  st = check_extents(fn, L, g, w, m_cap);
   if (st != CCA_OK) return st;
   st = check_pool_mode(fn, pool_mode, Hq, Hkv);
   if (st != CCA_OK) return st;
@@ -345,6 +366,8 @@ cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, c
   if (st != CCA_OK) return st;
   st = check_rows(fn, q_start, q_len, Lq, Lk);
   if (st != CCA_OK) return st;
+  st = check_extents(fn, Lq > Lk ? Lq : Lk, g, w, m_cap);
+  if (st != CCA_OK) return st;
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
   REQUIRE_PTR(v);
@@ -378,6 +401,8 @@ cca_status cca_cache_fill_ring(const void* k, const void* v, void* ring_k, void*
   cca_status st = check_heads(fn, B, Hkv, Hkv, d, dt);
   if (st != CCA_OK) return st;
   if (R < 1 || Lk < 1) return fail(CCA_ERR_INVALID_ARG, "%s: R=%d Lk=%d must be >= 1", fn, R, Lk);
+  st = check_extents(fn, Lk, -1, -1, R);
+  if (st != CCA_OK) return st;
   if (seq_len == nullptr || (reinterpret_cast<uintptr_t>(seq_len) & 3u) != 0)
     return fail(CCA_ERR_INVALID_ARG, "%s: seq_len is NULL or not 4-byte aligned", fn);
   REQUIRE_PTR(k);
@@ -419,6 +444,8 @@ cca_status attn_decode(const char* fn, const void* q_t, const void* k_t, const v
   st = check_pool_mode(fn, pool_mode, Hq, Hkv);
   if (st != CCA_OK) return st;
   st = check_out_dt(fn, out_dt, dt);
+  if (st != CCA_OK) return st;
+  st = check_extents(fn, R, g, w, m_cap);
   if (st != CCA_OK) return st;
   REQUIRE_PTR(q_t);
   REQUIRE_PTR(k_t);

@@ -32,8 +32,11 @@ constexpr int kBatch = 4;  // keys per lane group per iteration
 template <int DT>
 using Slice = Row16<DT>;  // a lane's 16-byte slice of a row, as floats
 
+// A step at position t runs when t >= 0, t + 1 does not overflow, and the
+// group that t completes has a core slot: (t+1)/g <= m_cap (which also bounds
+// every visible core, n_core(t) <= (t+1)/g).
 __device__ __forceinline__ bool decode_valid(int t, int g, int m_cap) {
-  return t >= 0 && (t + 1) / g <= m_cap;
+  return t >= 0 && t < 0x7fffffff && (t + 1) / g <= m_cap;
 }
 
 // Pools the group ending at t with one wave, in pooling mode `mode`: rows
@@ -568,7 +571,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
   }
   const float r = red[1] != 0.f ? NAN : osum / lsum;
   EO::store(static_cast<typename EO::T*>(out_), bh * D + e, r);
-  if (advance_pos && e == 0 && bh % Hq == 0) pos[bh / Hq] += 1;
+  if (advance_pos && e == 0 && bh % Hq == 0 && pos[bh / Hq] < 0x7fffffff) pos[bh / Hq] += 1;
 }
 
 int pick_gt(int G) {

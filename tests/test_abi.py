@@ -70,6 +70,7 @@ def decode(lib, q=FAKE, kt=FAKE, vt=FAKE, rk=FAKE, rv=FAKE, R=1024, ck=FAKE, cv=
     (dict(B=0), INV), (dict(Hq=0), INV), (dict(dt=7), INV), (dict(d=96), UNS), (dict(Hq=3), UNS),
     (dict(m_cap=63), CAP), (dict(ck=None), INV), (dict(wts=MIS), INV),
     (dict(B=1 << 16, Hq=1 << 10, Hkv=1 << 10, L=1 << 12, m_cap=256), UNS),
+    (dict(g=1 << 30), UNS), (dict(L=(1 << 30) + 1, d=64, Hq=2, Hkv=1, m_cap=1 << 30), UNS),
 ])
 def test_pool_validation(cca_lib, kw, code):
     assert pool(cca_lib, **kw) == code
@@ -85,6 +86,7 @@ def test_pool_without_complete_group_is_a_no_op(cca_lib):
     (dict(out=None), INV), (dict(w=0), INV), (dict(out_dt=5), INV), (dict(dt=0, out_dt=1), UNS),
     (dict(kernel=3), INV), (dict(dt=0, out_dt=0, kernel=2), UNS), (dict(d=32), UNS),
     (dict(Hkv=3), UNS), (dict(m_cap=10), CAP), (dict(cv=None), INV), (dict(q=MIS), INV),
+    (dict(w=(1 << 30) + 1), UNS), (dict(g=(1 << 30) + 1), UNS),
 ])
 def test_prefill_validation(cca_lib, kw, code):
     assert prefill(cca_lib, **kw) == code
@@ -94,7 +96,8 @@ def test_prefill_validation(cca_lib, kw, code):
     (dict(R=1023), CAP), (dict(R=8, w=4, g=16), CAP), (dict(ws_bytes=16), CAP), (dict(pos=None), INV),
     (dict(pos=FAKE + 2), INV), (dict(g=0), INV), (dict(w=0), INV), (dict(rk=None), INV),
     (dict(out_dt=0, dt=0, d=80), UNS), (dict(Hq=6, Hkv=4), UNS), (dict(m_cap=-1), INV),
-    (dict(ck=None), INV), (dict(ws=None), INV),
+    (dict(ck=None), INV), (dict(ws=None), INV), (dict(R=(1 << 30) + 1), UNS), (dict(g=(1 << 30) + 1), UNS),
+    (dict(m_cap=(1 << 30) + 1), UNS),
 ])
 def test_decode_validation(cca_lib, kw, code):
     assert decode(cca_lib, **kw) == code
@@ -160,6 +163,7 @@ def fill_ring(lib, k=FAKE, v=FAKE, rk=FAKE, rv=FAKE, R=1024, sl=FAKE, B=2, Hkv=2
     (dict(ck=None), INV), (dict(d=96), UNS), (dict(mode=1, Hq=18, Hkv=2), UNS),
     (dict(m_cap=0, ck=None, cv=None), OK),  # no core slot: nothing to do
     (dict(q=None, mode=_lib.CCA_POOL_MAX, m_cap=0), OK),
+    (dict(g=(1 << 30) + 1), UNS), (dict(Lk=(1 << 30) + 1, d=64, B=1, Hq=1, Hkv=1), UNS),
 ])
 def test_pool_chunk_validation(cca_lib, kw, code):
     assert pool_chunk(cca_lib, **kw) == code
@@ -168,7 +172,7 @@ def test_pool_chunk_validation(cca_lib, kw, code):
 @pytest.mark.parametrize("kw,code", [
     (dict(qs=None), INV), (dict(ql=None), INV), (dict(qs=FAKE + 1), INV), (dict(Lq=0), INV), (dict(w=0), INV),
     (dict(out=None), INV), (dict(m_cap=-1), INV), (dict(cv=None), INV), (dict(dt=0, out_dt=1), UNS),
-    (dict(Hkv=3), UNS), (dict(out_dt=4), INV),
+    (dict(Hkv=3), UNS), (dict(out_dt=4), INV), (dict(w=(1 << 30) + 1), UNS),
 ])
 def test_prefill_chunk_validation(cca_lib, kw, code):
     assert prefill_chunk(cca_lib, **kw) == code
@@ -176,7 +180,7 @@ def test_prefill_chunk_validation(cca_lib, kw, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(R=0), INV), (dict(Lk=0), INV), (dict(sl=None), INV), (dict(sl=FAKE + 2), INV), (dict(rk=None), INV),
-    (dict(d=32), UNS), (dict(B=1 << 9, Hkv=1 << 8), UNS),
+    (dict(d=32), UNS), (dict(B=1 << 9, Hkv=1 << 8), UNS), (dict(R=(1 << 30) + 1, B=1, Hkv=1), UNS),
 ])
 def test_fill_ring_validation(cca_lib, kw, code):
     assert fill_ring(cca_lib, **kw) == code
@@ -193,7 +197,8 @@ def test_decode_workspace_size(cca_lib):
     assert f(0, 32, 8, 128, 4112, 16, 1024) == 0
 
 
-@pytest.mark.parametrize("args,code", [((0, 16, 4), INV), ((10, 0, 4), INV), ((10, 4, 0), INV)])
+@pytest.mark.parametrize("args,code", [((0, 16, 4), INV), ((10, 0, 4), INV), ((10, 4, 0), INV),
+                                       ((10, 4, (1 << 30) + 1), UNS)])
 def test_visibility_validation(cca_lib, args, code):
     assert cca_lib.cca_visibility_table(*args, P(FAKE), P(FAKE), P(FAKE), None) == code
     assert cca_lib.cca_visibility_table(10, 4, 4, P(None), P(FAKE), P(FAKE), None) == INV

@@ -430,19 +430,20 @@ def test_decode_without_advancing_pos():
 
 
 def test_decode_out_of_capacity_gives_nan_and_no_writes():
-    say("decode capacity overflow")
-    B, Hq, Hkv, d, g, w, R, m_cap = 2, 4, 2, 128, 4, 8, 8, 3
+    say("decode capacity overflow, and a position whose successor overflows int32")
+    B, Hq, Hkv, d, g, w, R, m_cap = 3, 4, 2, 128, 4, 8, 8, 3
     mk = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device=DEV)
     q_t, k_t, v_t = mk(B, Hq, d) + 1, mk(B, Hkv, d) + 1, mk(B, Hkv, d) + 1
     rk, rv, ck, cv = mk(B, Hkv, R, d), mk(B, Hkv, R, d), mk(B, Hkv, m_cap, d), mk(B, Hkv, m_cap, d)
-    pos = torch.tensor([10, 15], dtype=torch.int32, device=DEV)   # (15+1)/4 = 4 > m_cap = 3
+    imax = 2 ** 31 - 1  # t + 1 would wrap to a negative group index
+    pos = torch.tensor([10, 15, imax], dtype=torch.int32, device=DEV)   # (15+1)/4 = 4 > m_cap = 3
     ws = torch.empty(cca.cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w), dtype=torch.uint8, device=DEV)
     out = mk(B, Hq, d)
     cca.cca_attn_decode(q_t, k_t, v_t, rk, rv, ck, cv, pos, out, ws, g, w, advance_pos=True)
     torch.cuda.synchronize()
-    assert torch.isfinite(out[0].float()).all() and torch.isnan(out[1].float()).all()
-    assert bool((rk[1] == 0).all()) and bool((ck[1] == 0).all())
-    assert pos.tolist() == [11, 16]
+    assert torch.isfinite(out[0].float()).all() and torch.isnan(out[1:].float()).all()
+    assert bool((rk[1:] == 0).all()) and bool((ck[1:] == 0).all())
+    assert pos.tolist() == [11, 16, imax]
 
 
 def test_decode_graph_replay_matches_eager():
