@@ -4,6 +4,11 @@ Argument marshalling only: torch tensors supply device pointers and the
 current HIP stream; every step of the computation runs in the library's HIP
 kernels.  There is no fallback: if libcca.so is missing or does not load,
 importing the entry points raises.
+
+The C ABI sees pointers and sizes only, so the binding checks what it cannot:
+every tensor's shape against the sizes passed, its dtype, that it is
+contiguous and that it lives on the same GPU as the others.  A mismatch raises
+CCAError before anything reaches the library.
 """
 from __future__ import annotations
 
@@ -97,6 +102,43 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+_FLOAT = (torch.float32, torch.bfloat16)
+
+
+def _expect(tensors) -> None:
+    """tensors: (name, tensor or None, shape, allowed dtypes or None) per argument.  Shapes
+    and dtypes are checked first, then that every tensor is a contiguous tensor on one GPU."""
+    dev = None
+    for name, t, shape, dtypes in tensors:
+        if t is None:
+            raise CCAError(CCA_ERR_INVALID_ARG, f"{name} is missing")
+        if tuple(t.shape) != tuple(shape):
+            raise CCAError(CCA_ERR_INVALID_ARG, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if dtypes is not None and t.dtype not in dtypes:
+            raise CCAError(CCA_ERR_INVALID_ARG, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    for name, t, _, _ in tensors:
+        if t.device.type != "cuda":
+            raise CCAError(CCA_ERR_INVALID_ARG, f"{name} is not a GPU tensor ({t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise CCAError(CCA_ERR_INVALID_ARG, f"{name} is on {t.device}, the others on {dev}")
+        if not t.is_contiguous():
+            raise CCAError(CCA_ERR_INVALID_ARG, f"{name} is not contiguous")
+
+
+def _dims(t, n, name):
+    if t is None or t.dim() != n:
+        raise CCAError(CCA_ERR_INVALID_ARG, f"{name} must be a {n}-d tensor")
+    return tuple(t.shape)
+
+
+def _workspace(name, t):
+    if t is None:
+        return []
+    return [(name, t, tuple(t.shape), None)]
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -112,6 +154,11 @@ def cca_version() -> int:
 
 def cca_visibility_table(L: int, g: int, w: int, n_core: torch.Tensor, win_lo: torch.Tensor,
                          group_last: torch.Tensor | None, stream=None) -> None:
+    i32 = (torch.int32,)
+    spec = [("n_core", n_core, (L,), i32), ("win_lo", win_lo, (L,), i32)]
+    if g > 0 and L // g > 0:  # group_last is not written (and may be None) when L < g
+        spec.append(("group_last", group_last, (L // g,), i32))
+    _expect(spec)
     _check(load().cca_visibility_table(L, g, w, _ptr(n_core), _ptr(win_lo), _ptr(group_last),
                                        _stream(stream)))
 
@@ -120,9 +167,16 @@ def cca_pool_core(q, k, v, core_k, core_v, g: int, weights=None, mode: int = CCA
                   stream=None) -> None:
     """q [B,Hq,L,d]; k, v [B,Hkv,L,d]; core_k, core_v [B,Hkv,m_cap,d]; weights fp32 [B,Hkv,L//g,g];
     mode: one of the CCA_POOL_* rules (q gives the shapes; the mean and max rules do not read it)."""
-    B, Hq, L, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, L, d = _dims(q, 4, "q")
+    Hkv = _dims(k, 4, "k")[1]
     m_cap = core_k.shape[2] if core_k is not None else 0
+    dt = (k.dtype,)
+    spec = [("q", q, (B, Hq, L, d), dt), ("k", k, (B, Hkv, L, d), _FLOAT), ("v", v, (B, Hkv, L, d), dt)]
+    if core_k is not None or core_v is not None:
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), dt), ("core_v", core_v, (B, Hkv, m_cap, d), dt)]
+    if weights is not None:
+        spec.append(("weights", weights, (B, Hkv, L // g if g > 0 else 0, g), (torch.float32,)))
+    _expect(spec)
     _check(load().cca_pool_core_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
                                    _ptr(weights), B, Hq, Hkv, L, d, g, _dt(k), mode, _stream(stream)))
 
@@ -130,12 +184,22 @@ def cca_pool_core(q, k, v, core_k, core_v, g: int, weights=None, mode: int = CCA
 def cca_attn_prefill(q, k, v, core_k, core_v, out, g: int, w: int, kernel: int = 0,
                      stream=None) -> None:
     """out [B,Hq,L,d] in q's dtype or fp32; kernel: 0 auto, 1 vector-ALU, 2 matrix-core."""
-    B, Hq, L, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, L, d = _dims(q, 4, "q")
+    Hkv = _dims(k, 4, "k")[1]
     m_cap = core_k.shape[2] if core_k is not None else 0
+    _expect(_attn_spec(q, k, v, core_k, core_v, out, B, Hq, Hkv, L, L, d, m_cap))
     _check(load().cca_attn_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
                                       _ptr(out), _dt(out), B, Hq, Hkv, L, d, g, w, _dt(q), kernel,
                                       _stream(stream)))
+
+
+def _attn_spec(q, k, v, core_k, core_v, out, B, Hq, Hkv, Lq, Lk, d, m_cap):
+    dt = (q.dtype,)
+    spec = [("q", q, (B, Hq, Lq, d), _FLOAT), ("k", k, (B, Hkv, Lk, d), dt), ("v", v, (B, Hkv, Lk, d), dt),
+            ("out", out, (B, Hq, Lq, d), (q.dtype, torch.float32))]
+    if core_k is not None or core_v is not None:
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), dt), ("core_v", core_v, (B, Hkv, m_cap, d), dt)]
+    return spec
 
 
 def cca_decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, m_cap: int, g: int, w: int) -> int:
@@ -148,10 +212,17 @@ def cca_attn_decode(q_t, k_t, v_t, ring_k, ring_v, core_k, core_v, pos, out, wor
     """q_t [B,Hq,d]; k_t, v_t [B,Hkv,d]; ring_* [B,Hkv,R,d]; core_* [B,Hkv,m_cap,d];
     pos int32 [B]; out [B,Hq,d]; workspace uint8 of cca_decode_workspace_bytes bytes;
     pool_mode: the CCA_POOL_* rule for the core appended when a group completes."""
-    B, Hq, d = q_t.shape
-    Hkv = k_t.shape[1]
-    R = ring_k.shape[2]
-    m_cap = core_k.shape[2]
+    B, Hq, d = _dims(q_t, 3, "q_t")
+    Hkv = _dims(k_t, 3, "k_t")[1]
+    R = _dims(ring_k, 4, "ring_k")[2]
+    m_cap = core_k.shape[2] if core_k is not None else 0
+    dt = (q_t.dtype,)
+    spec = [("q_t", q_t, (B, Hq, d), _FLOAT), ("k_t", k_t, (B, Hkv, d), dt), ("v_t", v_t, (B, Hkv, d), dt),
+            ("ring_k", ring_k, (B, Hkv, R, d), dt), ("ring_v", ring_v, (B, Hkv, R, d), dt),
+            ("pos", pos, (B,), (torch.int32,)), ("out", out, (B, Hq, d), (q_t.dtype, torch.float32))]
+    if core_k is not None or core_v is not None:
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), dt), ("core_v", core_v, (B, Hkv, m_cap, d), dt)]
+    _expect(spec + _workspace("workspace", workspace))
     _check(load().cca_attn_decode_ex(_ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(ring_k), _ptr(ring_v), R,
                                      _ptr(core_k), _ptr(core_v), m_cap, _ptr(pos), int(advance_pos),
                                      _ptr(out), _dt(out), _ptr(workspace),
@@ -170,9 +241,15 @@ def cca_pool_core_chunk(q, k, v, core_k, core_v, g: int, q_start, q_len,
     """Pools the groups completed by each sequence's chunk.  q [B,Hq,Lq,d] holds the chunk rows
     (local row i = position q_start[b] + i); k, v [B,Hkv,Lk,d] hold positions 0..; q_start, q_len
     int32 [B] on the device; core_k, core_v [B,Hkv,m_cap,d]."""
-    B, Hq, Lq, d = q.shape
-    Hkv, Lk = k.shape[1], k.shape[2]
-    m_cap = core_k.shape[2]
+    B, Hq, Lq, d = _dims(q, 4, "q")
+    _, Hkv, Lk, _ = _dims(k, 4, "k")
+    m_cap = core_k.shape[2] if core_k is not None else 0
+    dt = (k.dtype,)
+    spec = [("q", q, (B, Hq, Lq, d), dt), ("k", k, (B, Hkv, Lk, d), _FLOAT), ("v", v, (B, Hkv, Lk, d), dt),
+            ("q_start", q_start, (B,), (torch.int32,)), ("q_len", q_len, (B,), (torch.int32,))]
+    if core_k is not None or core_v is not None:
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), dt), ("core_v", core_v, (B, Hkv, m_cap, d), dt)]
+    _expect(spec)
     _check(load().cca_pool_core_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
                                       _rows(q_start), _rows(q_len), B, Hq, Hkv, Lq, Lk, d, g, _dt(k),
                                       mode, _stream(stream)))
@@ -182,9 +259,11 @@ def cca_attn_prefill_chunk(q, k, v, core_k, core_v, out, g: int, w: int, q_start
                            stream=None) -> None:
     """Fused attention rows of each sequence's chunk (see cca_pool_core_chunk for the layout);
     out [B,Hq,Lq,d] in q's dtype or fp32."""
-    B, Hq, Lq, d = q.shape
-    Hkv, Lk = k.shape[1], k.shape[2]
+    B, Hq, Lq, d = _dims(q, 4, "q")
+    _, Hkv, Lk, _ = _dims(k, 4, "k")
     m_cap = core_k.shape[2] if core_k is not None else 0
+    _expect(_attn_spec(q, k, v, core_k, core_v, out, B, Hq, Hkv, Lq, Lk, d, m_cap) +
+            [("q_start", q_start, (B,), (torch.int32,)), ("q_len", q_len, (B,), (torch.int32,))])
     _check(load().cca_attn_prefill_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
                                          _ptr(out), _dt(out), _rows(q_start), _rows(q_len), B, Hq, Hkv,
                                          Lq, Lk, d, g, w, _dt(q), _stream(stream)))
@@ -193,19 +272,23 @@ def cca_attn_prefill_chunk(q, k, v, core_k, core_v, out, g: int, w: int, q_start
 def cca_cache_fill_ring(k, v, ring_k, ring_v, seq_len, stream=None) -> None:
     """Copies the last R positions below seq_len[b] of k, v [B,Hkv,Lk,d] into ring slot p % R
     of ring_k, ring_v [B,Hkv,R,d]."""
-    B, Hkv, Lk, d = k.shape
-    R = ring_k.shape[2]
+    B, Hkv, Lk, d = _dims(k, 4, "k")
+    R = _dims(ring_k, 4, "ring_k")[2]
+    dt = (k.dtype,)
+    _expect([("k", k, (B, Hkv, Lk, d), _FLOAT), ("v", v, (B, Hkv, Lk, d), dt),
+             ("ring_k", ring_k, (B, Hkv, R, d), dt), ("ring_v", ring_v, (B, Hkv, R, d), dt),
+             ("seq_len", seq_len, (B,), (torch.int32,))])
     _check(load().cca_cache_fill_ring(_ptr(k), _ptr(v), _ptr(ring_k), _ptr(ring_v), R, _rows(seq_len),
                                       B, Hkv, Lk, d, _dt(k), _stream(stream)))
 
 
 def cca_attn_prefill_train(q, k, v, core_k, core_v, out, lse, g: int, w: int, stream=None) -> None:
     """cca_attn_prefill that also writes lse fp32 [B,Hq,L], each row's log-sum-exp of its scores."""
-    B, Hq, L, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, L, d = _dims(q, 4, "q")
+    Hkv = _dims(k, 4, "k")[1]
     m_cap = core_k.shape[2] if core_k is not None else 0
-    if lse.dtype != torch.float32:
-        raise CCAError(CCA_ERR_INVALID_ARG, "lse must be fp32")
+    _expect(_attn_spec(q, k, v, core_k, core_v, out, B, Hq, Hkv, L, L, d, m_cap) +
+            [("lse", lse, (B, Hq, L), (torch.float32,))])
     _check(load().cca_attn_prefill_train(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
                                          _ptr(out), _dt(out), _ptr(lse), B, Hq, Hkv, L, d, g, w, _dt(q),
                                          _stream(stream)))
@@ -219,12 +302,15 @@ def cca_attn_backward(q, k, v, core_k, core_v, out, lse, dout, dq, dk, dv, works
                       pool_mode: int = CCA_POOL_SOFTMAX, stream=None) -> None:
     """Gradients dq [B,Hq,L,d], dk, dv [B,Hkv,L,d] (fp32, overwritten) of the forward (pooling with
     rule pool_mode, then the fused prefill) for the upstream gradient dout of out."""
-    B, Hq, L, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, L, d = _dims(q, 4, "q")
+    Hkv = _dims(k, 4, "k")[1]
     m_cap = core_k.shape[2] if core_k is not None else 0
-    for t in (dq, dk, dv):
-        if t.dtype != torch.float32:
-            raise CCAError(CCA_ERR_INVALID_ARG, "gradients are fp32")
+    f32 = (torch.float32,)
+    spec = _attn_spec(q, k, v, core_k, core_v, out, B, Hq, Hkv, L, L, d, m_cap)
+    spec[3] = ("out", out, (B, Hq, L, d), (q.dtype,))
+    _expect(spec + [("lse", lse, (B, Hq, L), f32), ("dout", dout, (B, Hq, L, d), (q.dtype,)),
+                    ("dq", dq, (B, Hq, L, d), f32), ("dk", dk, (B, Hkv, L, d), f32),
+                    ("dv", dv, (B, Hkv, L, d), f32)] + _workspace("workspace", workspace))
     _check(load().cca_attn_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap, _ptr(out),
                                     _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), B, Hq, Hkv, L, d, g, w,
