@@ -36,16 +36,12 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 
 
-def measured_traffic(name):
-    """HBM bytes per launch from a committed counter summary under profiles/.
-
-    The summary holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch) scaled by
-    what the same counters read for a device copy of known size, plus a
-    digest of the kernel's sources; if their code has changed since the
-    counters were taken the figure no longer describes the kernel and None is
-    returned.
-    """
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+def profile_fields(filename):
+    """The `key: value` lines of a committed counter summary under profiles/,
+    or None when the summary is missing or its kernel has changed since the
+    counters were taken (the summary carries a digest of the kernel's sources
+    and build flags; a figure for other code describes nothing here)."""
+    path = os.path.join(ROOT, "profiles", filename)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -58,9 +54,23 @@ def measured_traffic(name):
         digest = code_digest(fields.get("sources", "").split())
     except OSError:
         return None
-    if digest != fields.get("kernel_sha256"):
-        return None
-    return int(fields["traffic_bytes"])
+    return fields if digest == fields.get("kernel_sha256") else None
+
+
+def measured_traffic(name):
+    """HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a device copy of known
+    size (profiles/traffic_<name>.txt)."""
+    fields = profile_fields(f"traffic_{name}.txt")
+    return int(fields["traffic_bytes"]) if fields else None
+
+
+def measured_mfma_busy(name, kernel="mfma_busy_fraction"):
+    """Fraction of SIMD cycles with the matrix cores busy, from the shader
+    counters in profiles/counters_<name>.txt (it includes masked and
+    recomputed work, unlike the algorithmic fraction)."""
+    fields = profile_fields(f"counters_{name}.txt")
+    return float(fields[kernel]) if fields and kernel in fields else None
 
 
 def code_digest(sources):
@@ -202,6 +212,8 @@ def bench_backward(cca, cfg, qd, kd, vd, steps=2, warmup=1):
     return {"workload": cfg.name, "steps": steps, "ms_per_call": ms, "algorithmic_flops": flops,
             "achieved_TFLOP_per_s": tflops, "bound": "mfma", "peak": PEAK_BF16_TFLOPS,
             "frac": tflops / PEAK_BF16_TFLOPS, "executed_mfma_flops": 14.0 * d * pairs,
+            "mfma_busy": {k: measured_mfma_busy("backward_mfma_gqa_L131072", f"{k}_mfma_busy_fraction")
+                          for k in ("dq", "dkv")},
             "note": "bf16 matrix-core kernels (fp32 accumulate); gradients fp32"}
 
 
@@ -413,6 +425,7 @@ def main():
             "frac": tflops / PEAK_BF16_TFLOPS,
             "traffic": measured_traffic("prefill_mfma_gqa_L131072"),
             "traffic_unit": "bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "mfma_busy": measured_mfma_busy("prefill_mfma_gqa_L131072"),
             "algorithmic_flops_per_launch": flops,
             "avg_launch_ms": prefill_avg,
         },
