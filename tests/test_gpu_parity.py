@@ -224,6 +224,33 @@ def test_prefill_is_deterministic():
     assert torch.equal(a, b)
 
 
+def test_pool_and_prefill_run_on_the_callers_stream():
+    """Work goes to the stream the call is made on.  On a side stream, a long
+    sleep precedes the writes of the inputs; pooling and prefill follow on the
+    same stream with no synchronisation in between.  Launches on any other
+    stream would read the inputs before they are written."""
+    B, Hq, Hkv, L, d, g, w = 1, 4, 2, 1000, 128, 16, 64
+    say(f"prefill on a side stream B={B} Hq={Hq} Hkv={Hkv} L={L}")
+    cfg = cfg_of("stream", B, Hq, Hkv, L, d, g, w, "bf16", seed=77)
+    (q, k, v), ref = run_prefill(cfg, 0, "bf16")
+    torch.cuda.synchronize()
+    qh, kh, vh = (x.pin_memory() for x in (q, k, v))
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        qd = torch.zeros(q.shape, dtype=q.dtype, device=DEV)
+        kd = torch.zeros(k.shape, dtype=k.dtype, device=DEV)
+        vd = torch.zeros(v.shape, dtype=v.dtype, device=DEV)
+        torch.cuda._sleep(50_000_000)  # tens of milliseconds of GPU time on this stream
+        qd.copy_(qh, non_blocking=True)
+        kd.copy_(kh, non_blocking=True)
+        vd.copy_(vh, non_blocking=True)
+        ck, cv, _ = gpu_pool(qd, kd, vd, g)
+        out = torch.full(q.shape, float("nan"), dtype=q.dtype, device=DEV)
+        cca.cca_attn_prefill(qd, kd, vd, ck, cv, out, g, w)
+    side.synchronize()
+    assert torch.equal(out, ref)
+
+
 def sample_rows(L, g, w, rng, n_random=40):
     rows = {0, 1, L - 1, L - 2, L // 2}
     for base in (w - 1, w, w + 1, w + g - 1, w + g, 2 * w + 3 * g - 1, L - w, L - w - 1):
