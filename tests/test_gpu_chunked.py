@@ -203,3 +203,42 @@ def test_prefill_decode_handoff(dt):
     say(f"  max abs err over steps {worst:.3e}")
     assert worst <= TOL[dt]
     assert pos.tolist() == [p + steps for p in lens]
+
+
+def test_chunked_full_size_is_bit_identical_to_full_prefill():
+    """The 128K GQA workload in five ragged chunks (boundaries off every tile
+    and group edge) gives the one-shot prefill's outputs and cores bit for bit:
+    a row's result depends only on the keys it sees, the key tiles sit at
+    absolute 64-key boundaries in both runs, and a key outside a row's sets
+    adds exact zeros.  (The one-shot prefill itself is checked against the
+    oracle at this size in test_gpu_parity.)"""
+    cfg = cca_inputs.CONFIGS[4]
+    chunks = [1, 20000, 32768, 45679, 32624]
+    assert sum(chunks) == cfg.L
+    say(f"chunked vs one-shot prefill at full size {cfg.name}, chunks {chunks}")
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    del q, k, v
+    B, Hkv, d, g, w = cfg.B, cfg.Hkv, cfg.d, cfg.g, cfg.w
+    m = cfg.L // g
+    ck_full = torch.empty((B, Hkv, m, d), dtype=qd.dtype, device=DEV)
+    cv_full = torch.empty_like(ck_full)
+    out_full = torch.empty_like(qd)
+    cca.cca_pool_core(qd, kd, vd, ck_full, cv_full, g)
+    cca.cca_attn_prefill(qd, kd, vd, ck_full, cv_full, out_full, g, w)
+    ck = torch.full_like(ck_full, float("nan"))
+    cv = torch.full_like(ck_full, float("nan"))
+    out = torch.full_like(qd, float("nan"))
+    start = 0
+    for C in chunks:
+        qc = qd[:, :, start:start + C].contiguous()
+        qs, ql = i32([start] * B), i32([C] * B)
+        oc = torch.empty((B, cfg.Hq, C, d), dtype=qd.dtype, device=DEV)
+        cca.cca_pool_core_chunk(qc, kd, vd, ck, cv, g, qs, ql)
+        cca.cca_attn_prefill_chunk(qc, kd, vd, ck, cv, oc, g, w, qs, ql)
+        out[:, :, start:start + C] = oc
+        start += C
+    torch.cuda.synchronize()
+    assert torch.equal(ck, ck_full) and torch.equal(cv, cv_full), "cores differ"
+    same = out == out_full
+    assert bool(same.all()), f"{int((~same).sum())} output values differ"
