@@ -135,8 +135,8 @@ void dq_mfma_kernel(DqParams P) {
   const int t = min(t_raw, L - 1);
   const int my_nc = n_core(t, g, w), my_lo = win_lo(t, w);
   const int w_lo = uni(min(row0, L - 1)), w_hi = uni(min(row0 + 31, L - 1));
-  const int wnc_lo = uni(n_core(w_lo, g, w)), wnc_hi = uni(n_core(w_hi, g, w));
-  const int wlo_lo = uni(win_lo(w_lo, w)), wlo_hi = uni(win_lo(w_hi, w));
+  const int wnc_lo = uni(n_core(w_lo, g, w));
+  const int wlo_hi = uni(win_lo(w_hi, w));
   const int nc_hi = uni(n_core(P_hi, g, w));
   const int n_ct = (nc_hi + kTileRows - 1) / kTileRows;
   const int r0 = win_lo(P_lo, w) & ~(kTileRows - 1);
@@ -364,7 +364,7 @@ template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkv_mfma_kernel(DkvParams P) {
   constexpr int NW = 8;
-  constexpr int KS = D / 16, DB = D / 32, DBH = DB / 2;
+  constexpr int KS = D / 16, DB = D / 32;
   typedef BothWaysTile<D> RT;  // Q and dO tiles: row reads and transposing reads
   // The row statistics of a tile (64 x 8 bytes) sit in the Q tile's unused tail.
   static_assert(RT::kBytes - RT::kBytesUsed >= 512, "room for the row statistics");

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
   const long st_base = ((long)b * Hq + h0) * splits + split;  // state of head h0
 
   if (!decode_valid(t, g, m_cap)) {
-    if (threadIdx.x < G) ws_m[st_base + (long)threadIdx.x * splits] = NAN;
+    if ((int)threadIdx.x < G) ws_m[st_base + (long)threadIdx.x * splits] = NAN;
     return;
   }
   const long bkl = bk;

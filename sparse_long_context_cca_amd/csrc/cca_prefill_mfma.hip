@@ -151,8 +151,8 @@ void prefill_mfma_kernel(PrefillParams P) {
   auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
   const int w_lo = uni(min(p0, Le - 1));
   const int w_hi = uni(min(p0 + 31, Le - 1));
-  const int wnc_lo = uni(n_core(w_lo, g, w)), wnc_hi = uni(n_core(w_hi, g, w));
-  const int wlo_lo = uni(win_lo(w_lo, w)), wlo_hi = uni(win_lo(w_hi, w));
+  const int wnc_lo = uni(n_core(w_lo, g, w));
+  const int wlo_hi = uni(win_lo(w_hi, w));
 
   // ---- workgroup key range
   const int nc_hi = uni(n_core(P_hi, g, w));
