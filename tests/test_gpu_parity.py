@@ -174,6 +174,8 @@ PREFILL_CASES = [
     (1, 4, 4, 4096, 128, 16, 1024),
     (1, 16, 8, 3000, 128, 16, 512),
     (2, 2, 1, 161, 128, 64, 2),
+    (1, 32, 2, 1500, 128, 16, 300),   # G = 16: two head groups of 8 per kv head
+    (1, 12, 1, 900, 64, 16, 128),     # G = 12: head groups of 4
 ]
 
 
@@ -423,6 +425,8 @@ DECODE_CASES = [
     ("bf16", 128, 2, 4, 1, 16, 1024, 1024, [3000, 1100], 33, 256),
     ("bf16", 64, 1, 2, 2, 3, 5, 7, [50], 30, 40),
     ("f32", 128, 2, 16, 2, 16, 128, 160, [1, 700], 50, 64),
+    ("bf16", 128, 2, 32, 2, 16, 64, 64, [200, 901], 20, 128),   # G = 16: the vector-ALU split kernel in bf16
+    ("bf16", 64, 1, 12, 1, 4, 16, 16, [33], 25, 64),             # G = 12
 ]
 
 
