@@ -101,6 +101,7 @@ POOL_CASES = [
     # B, Hq, Hkv, L, d, g
     (1, 1, 1, 16, 64, 16), (2, 4, 2, 37, 128, 3), (1, 8, 1, 300, 128, 16), (1, 2, 2, 97, 64, 1),
     (1, 3, 1, 50, 128, 7), (2, 4, 4, 1024, 128, 16), (1, 6, 3, 129, 64, 40),
+    (1, 32, 2, 200, 128, 16), (1, 4, 1, 700, 64, 64),
 ]
 
 
