@@ -310,7 +310,7 @@ def test_prefill_full_size(number):
     rng = np.random.default_rng(number)
     rows = sample_rows(cfg.L, cfg.g, cfg.w, rng)
     worst = {"f32 out": 0.0, "bf16 out": 0.0, "bf16 out beyond its rounding": 0.0,
-             "f32 out vs unrounded cores": 0.0}
+             "f32 out vs unrounded cores": 0.0, "oracle itself, rounded vs unrounded cores": 0.0}
 
     def check(hsl, rsl, ref, ref_unrounded):
         g32 = host(out_f32[:, hsl, rsl])
@@ -318,14 +318,16 @@ def test_prefill_full_size(number):
         d16 = np.abs(host(out_bf[:, hsl, rsl]) - ref)
         e16, x16 = float(d16.max()), float((d16 - bf16_half_ulp(ref)).max())
         eu = float(np.abs(g32 - ref_unrounded).max())
-        for key, val in zip(worst, (e32, e16, x16, eu)):
+        eo = float(np.abs(ref - ref_unrounded).max())
+        for key, val in zip(worst, (e32, e16, x16, eu, eo)):
             worst[key] = max(worst[key], val)
-        return e32, e16, x16, eu
+        return e32, e16, x16, eu, eo
 
     def stored(x):  # the storage dtype's rounding (RNE), widened back exactly
         return torch.from_numpy(x).to(q.dtype).to(torch.float64).numpy()
 
-    line = "    max abs err: f32 out %.3e, bf16 out %.3e (%.3e beyond its rounding); vs unrounded cores %.3e"
+    line = ("    max abs err: f32 out %.3e, bf16 out %.3e (%.3e beyond its rounding); vs unrounded cores %.3e"
+            " (the oracle itself moves by %.3e)")
 
     for hk in kv_heads:
         heads = list(range(hk * G, hk * G + G))
@@ -343,7 +345,7 @@ def test_prefill_full_size(number):
             continue
         for r0, r1 in dense_blocks(cfg.L):
             say(f"  oracle kv head {hk}, every row of {r0}..{r1 - 1}")
-            e = [0.0, 0.0, 0.0, 0.0]
+            e = [0.0] * 5
             for t0 in range(r0, r1, 128):
                 t1 = min(r1, t0 + 128)
                 ref = orc.attn_rows_masked(Qh, K, V, CKs, CVs, cfg.g, cfg.w, t0, t1)
