@@ -292,7 +292,8 @@ def test_prefill_full_size(number):
     alone moves the oracle's own outputs by ~0.025.
     The first kv head's query heads (a whole kv-head group) are checked on
     every row (the oracle's masked multi-row form, 128 rows at a time) and on
-    sampled rows; the last kv head's on the sampled rows."""
+    sampled rows; the last kv head's on the sampled rows.  Every core of both
+    kv heads is checked against the oracle's pooling too."""
     cfg = cca_inputs.CONFIGS[number]
     say(f"prefill full-size config {cfg.name}: generating inputs")
     q, k, v = cca_inputs.prefill_inputs(cfg)
@@ -336,6 +337,9 @@ def test_prefill_full_size(number):
         V = f32np(v[:, hk : hk + 1])
         Qh = f32np(q[:, hsl])
         CK, CV, _ = orc.pool_core(Qh, K, V, cfg.g)
+        say(f"  cores of kv head {hk}: all {CK.shape[2]} against the oracle")
+        check_cores(cfg.dtype, ck[:, hk : hk + 1], CK, cca.CCA_POOL_SOFTMAX)
+        check_cores(cfg.dtype, cv[:, hk : hk + 1], CV, cca.CCA_POOL_SOFTMAX)
         CKs, CVs = stored(CK), stored(CV)
         say(f"  oracle kv head {hk} (query heads {heads[0]}..{heads[-1]}), {len(rows)} sampled rows")
         ref = orc.attn_rows(Qh, K, V, CKs, CVs, cfg.g, cfg.w, rows)
