@@ -129,6 +129,47 @@ def attn_backward_rows(Q, K, V, CK, CV, g: int, w: int, dO, rows):
     return dQ, dK, dV, dCK, dCV
 
 
+def attn_backward_rows_masked(Q, K, V, CK, CV, g: int, w: int, dO, t0: int, t1: int):
+    """Step 1 for the consecutive rows t0..t1-1, evaluated together.
+
+    The chain rule of ``attn_backward_rows`` written with a mask, for checking
+    every row of a long sequence: each row of the range is scored against the
+    cores 0..NC-1 and the raw positions LO..t1-1 (the union of the rows'
+    visible sets); keys outside a row's own sets get score -inf, hence P = 0
+    and dS = 0, so they neither give to dq nor receive from the row.  Returns
+    dQ [B,Hq,t1-t0,d] of the rows, their contributions to the raw keys
+    LO..t1-1, dK, dV [B,Hkv,t1-LO,d], and to the cores 0..NC-1, dCK, dCV
+    [B,Hkv,NC,d] (summed over the G query heads of each kv head), and LO; fp64.
+    """
+    B, Hq, _, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    ts = np.arange(t0, t1)
+    n = len(ts)
+    nc = np.array([n_core(int(t), g, w) for t in ts])
+    lo = np.array([win_lo(int(t), w) for t in ts])
+    NC, LO = int(nc.max()), int(lo.min())
+    scale = _scale(d)
+    q = _f64(Q[:, :, t0:t1]).reshape(B, Hkv, G, n, d)      # head h -> kv head h // G
+    go = _f64(dO[:, :, t0:t1]).reshape(B, Hkv, G, n, d)
+    ck, cv = _f64(CK[:, :, None, :NC]), _f64(CV[:, :, None, :NC])
+    kw, vw = _f64(K[:, :, None, LO:t1]), _f64(V[:, :, None, LO:t1])
+    sw = lambda x: np.swapaxes(x, -1, -2)
+    raw_pos = np.arange(LO, t1)[None, :]
+    vis = np.concatenate([np.arange(NC)[None, :] < nc[:, None],
+                          (raw_pos >= lo[:, None]) & (raw_pos <= ts[:, None])], axis=-1)
+    s = np.concatenate([q @ sw(ck), q @ sw(kw)], axis=-1) * scale
+    p = _softmax(np.where(vis, s, -np.inf))                   # one softmax over [cores ; window]
+    dp = np.concatenate([go @ sw(cv), go @ sw(vw)], axis=-1)
+    ds = _softmax_backward(p, dp)                             # [B,Hkv,G,n,NC + window]
+    dQ = ((ds[..., :NC] @ ck + ds[..., NC:] @ kw) * scale).reshape(B, Hq, n, d)
+    dCK = (sw(ds[..., :NC]) @ q).sum(axis=2) * scale
+    dCV = (sw(p[..., :NC]) @ go).sum(axis=2)
+    dK = (sw(ds[..., NC:]) @ q).sum(axis=2) * scale
+    dV = (sw(p[..., NC:]) @ go).sum(axis=2)
+    return dQ, dK, dV, dCK, dCV, LO
+
+
 def pool_backward(Q, K, V, g: int, dCK, dCV, mode: str = "softmax"):
     """Gradients of pooling (step 2) for upstream dCK, dCV [B,Hkv,m,d].
 

@@ -115,14 +115,14 @@ def test_backward_is_deterministic_where_no_atomics():
     assert torch.equal(a[0], b[0])
 
 
-def test_backward_full_size_sampled():
+def test_backward_full_size():
     """The 128K GQA workload (B1, 32/8 heads, d128, g16, w1024) at full size, in
     the launch configuration the benchmark times.  Checked against the oracle
-    for one kv head (its 4 query heads) where every contribution can be
-    summed cheaply: dq at every row of the last w + 3g positions and at rows
-    deep in the sequence that end no group; dk, dv at positions of the last
-    groups, whose raw-key rows and whose core's rows (the pooling share) all
-    lie in that range."""
+    for one kv head and its 4 query heads on everything: dq at every row, dk
+    and dv at every position, each with its pooling share.  The oracle runs
+    the masked multi-row form 128 rows at a time, sums the rows'
+    contributions to the raw keys and the cores, then the pooling backward
+    over the whole sequence (about a minute on 16 host cores)."""
     cfg = cca_inputs.CONFIGS[4]
     B, Hq, Hkv, L, d, g, w = cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.g, cfg.w
     G = Hq // Hkv
@@ -144,32 +144,35 @@ def test_backward_full_size_sampled():
     ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g), dtype=torch.uint8, device=DEV)
     cca.cca_attn_backward(qd, kd, vd, ck, cv, out, lse, gd, dq, dk, dv, ws, g, w)
     torch.cuda.synchronize()
-    r0 = L - w - 3 * g
-    deep = [t for t in (w + 5, L // 2 + 1, L // 2 + 2 * g + 7) if t % g != g - 1]
-    rows = deep + list(range(r0, L))
-    pos = [r0, r0 + g - 1, r0 + 2 * g + 3, L - w - 1, L - w, L - 700, L - g, L - 2, L - 1]
     hk = 0
     heads = slice(hk * G, hk * G + G)
-    dq_gpu = dq[:, heads, rows].double().cpu().numpy()
-    dk_gpu = dk[:, hk : hk + 1, pos].double().cpu().numpy()
-    dv_gpu = dv[:, hk : hk + 1, pos].double().cpu().numpy()
+    dq_gpu = dq[:, heads].double().cpu().numpy()
+    dk_gpu = dk[:, hk : hk + 1].double().cpu().numpy()
+    dv_gpu = dv[:, hk : hk + 1].double().cpu().numpy()
     del qd, kd, vd, gd, out, dq, dk, dv, ws
-    say(f"  oracle: kv head {hk}, {len(rows)} rows, {len(pos)} key positions")
+    say(f"  oracle: kv head {hk}, every row and every key position")
     Qh, Kh, Vh, Gh = f32np(q[:, heads]), f32np(k[:, hk : hk + 1]), f32np(v[:, hk : hk + 1]), f32np(dO[:, heads])
     CK, CV, _ = orc.pool_core(Qh, Kh, Vh, g)
-    dQr, dK, dV, dCK, dCV = bwd.attn_backward_rows(Qh, Kh, Vh, CK, CV, g, w, Gh, rows)
-    # pooling share of the last groups (those of every row from r0 on): the
-    # groups are independent, so pool_backward runs on the slice from group j0
-    j0 = r0 // g
-    pQ, pK, pV = bwd.pool_backward(Qh[:, :, j0 * g :], Kh[:, :, j0 * g :], Vh[:, :, j0 * g :], g,
-                                   dCK[:, :, j0:], dCV[:, :, j0:], "softmax")
-    dq_ref = dQr.copy()
-    for i, t in enumerate(rows):
-        if t >= j0 * g:
-            dq_ref[:, :, i] += pQ[:, :, t - j0 * g]
-    dk_ref = dK[:, :, pos] + pK[:, :, [p - j0 * g for p in pos]]
-    dv_ref = dV[:, :, pos] + pV[:, :, [p - j0 * g for p in pos]]
+    dq_ref = np.zeros((B, G, L, d))
+    dk_ref, dv_ref = np.zeros((B, 1, L, d)), np.zeros((B, 1, L, d))
+    dCK, dCV = np.zeros((B, 1, m, d)), np.zeros((B, 1, m, d))
+    for t0 in range(0, L, 128):
+        t1 = min(L, t0 + 128)
+        q_, k_, v_, ck_, cv_, lo = bwd.attn_backward_rows_masked(Qh, Kh, Vh, CK, CV, g, w, Gh, t0, t1)
+        dq_ref[:, :, t0:t1] = q_
+        dk_ref[:, :, lo:t1] += k_
+        dv_ref[:, :, lo:t1] += v_
+        dCK[:, :, : ck_.shape[2]] += ck_
+        dCV[:, :, : cv_.shape[2]] += cv_
+        if t1 % 16384 == 0:
+            say(f"    rows up to {t1}")
+    say("  oracle: pooling backward")
+    pQ, pK, pV = bwd.pool_backward(Qh, Kh, Vh, g, dCK, dCV, "softmax")
+    dq_ref += pQ
+    dk_ref += pK
+    dv_ref += pV
     for name, x, y in (("dq", dq_gpu, dq_ref), ("dk", dk_gpu, dk_ref), ("dv", dv_gpu, dv_ref)):
-        e = float(np.abs(x - y).max()) / max(1.0, float(np.abs(y).max()))
-        say(f"  {name} max err / scale {e:.3e} (scale {max(1.0, float(np.abs(y).max())):.2f})")
+        scale = max(1.0, float(np.abs(y).max()))
+        e = float(np.abs(x - y).max()) / scale
+        say(f"  {name} max err / scale {e:.3e} (scale {scale:.2f})")
         assert e <= TOL["bf16"], name

@@ -144,7 +144,35 @@ def pin_rows_form(b):
     return fails
 
 
-PINS = [pin_finite_differences, pin_reduces_to_causal_attention, pin_row_lse, pin_rows_form]
+def pin_masked_rows_form(b):
+    """The masked multi-row form, its contributions summed over runs of rows
+    that start and end anywhere, equals the per-row form over all rows."""
+    fails = []
+    for ci, (B, Hq, Hkv, L, d, g, w, n) in enumerate([(1, 4, 2, 37, 8, 3, 7, 5), (2, 2, 2, 29, 4, 4, 5, 8),
+                                                      (1, 3, 1, 20, 4, 1, 2, 20), (1, 2, 1, 45, 4, 6, 30, 7)]):
+        Q, K, V = _rand(540 + ci, (B, Hq, L, d)), _rand(550 + ci, (B, Hkv, L, d)), _rand(560 + ci, (B, Hkv, L, d))
+        dO = _rand(570 + ci, (B, Hq, L, d))
+        CK, CV, _ = orc.pool_core(Q, K, V, g)
+        ref = b.attn_backward_rows(Q, K, V, CK, CV, g, w, dO, range(L))
+        dQ = np.zeros_like(ref[0])
+        dK, dV, dCK, dCV = (np.zeros_like(x) for x in ref[1:])
+        for t0 in range(0, L, n):
+            t1 = min(L, t0 + n)
+            q_, k_, v_, ck_, cv_, LO = b.attn_backward_rows_masked(Q, K, V, CK, CV, g, w, dO, t0, t1)
+            dQ[:, :, t0:t1] = q_
+            dK[:, :, LO:t1] += k_
+            dV[:, :, LO:t1] += v_
+            dCK[:, :, : ck_.shape[2]] += ck_
+            dCV[:, :, : cv_.shape[2]] += cv_
+        for name, x, y in zip(("dQ", "dK", "dV", "dCK", "dCV"), (dQ, dK, dV, dCK, dCV), ref):
+            e = _close(x, y, 1e-12)
+            if e:
+                fails.append(f"case {ci} {name}: {e}")
+    return fails
+
+
+PINS = [pin_finite_differences, pin_reduces_to_causal_attention, pin_row_lse, pin_rows_form,
+        pin_masked_rows_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -188,6 +216,18 @@ def _attn_dv_from_ds(Q, K, V, CK, CV, g, w, dO):
     return dQ, dV, dK, dCK, dCV
 
 
+_ORIG_MASKED = bwd.attn_backward_rows_masked
+
+
+def _masked_window_one_long(Q, K, V, CK, CV, g, w, dO, t0, t1):
+    return _ORIG_MASKED(Q, K, V, CK, CV, g, w + 1, dO, t0, t1)
+
+
+def _masked_dv_from_ds(Q, K, V, CK, CV, g, w, dO, t0, t1):
+    dQ, dK, dV, dCK, dCV, LO = _ORIG_MASKED(Q, K, V, CK, CV, g, w, dO, t0, t1)
+    return dQ, dV, dK, dCK, dCV, LO
+
+
 MUTATIONS = {
     "softmax Jacobian without the row correction": ("_softmax_backward", lambda p, dp: p * dp),
     "backward scores not scaled by 1/sqrt(d)": ("_scale", lambda d: 1.0),
@@ -196,6 +236,8 @@ MUTATIONS = {
     "max-pooling gradient routed to the minimum": ("pool_backward", _pool_max_routes_to_min),
     "mean-pooling gradient divided by g-1": ("pool_backward", _pool_mean_over_g_minus_1),
     "raw dK and dV swapped": ("attn_backward", _attn_dv_from_ds),
+    "masked rows: window one token long": ("attn_backward_rows_masked", _masked_window_one_long),
+    "masked rows: raw dK and dV swapped": ("attn_backward_rows_masked", _masked_dv_from_ds),
 }
 
 
