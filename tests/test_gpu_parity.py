@@ -101,7 +101,7 @@ POOL_CASES = [
     # B, Hq, Hkv, L, d, g
     (1, 1, 1, 16, 64, 16), (2, 4, 2, 37, 128, 3), (1, 8, 1, 300, 128, 16), (1, 2, 2, 97, 64, 1),
     (1, 3, 1, 50, 128, 7), (2, 4, 4, 1024, 128, 16), (1, 6, 3, 129, 64, 40),
-    (1, 32, 2, 200, 128, 16), (1, 4, 1, 700, 64, 64),
+    (1, 32, 2, 200, 128, 16), (1, 4, 1, 700, 64, 64), (1, 4, 2, 450, 128, 100), (2, 2, 1, 133, 64, 33),
 ]
 
 
@@ -177,6 +177,7 @@ PREFILL_CASES = [
     (2, 2, 1, 161, 128, 64, 2),
     (1, 32, 2, 1500, 128, 16, 300),   # G = 16: two head groups of 8 per kv head
     (1, 12, 1, 900, 64, 16, 128),     # G = 12: head groups of 4
+    (1, 4, 2, 1300, 128, 100, 150),   # g = 100
 ]
 
 
@@ -433,6 +434,7 @@ DECODE_CASES = [
     ("f32", 128, 2, 16, 2, 16, 128, 160, [1, 700], 50, 64),
     ("bf16", 128, 2, 32, 2, 16, 64, 64, [200, 901], 20, 128),   # G = 16: the vector-ALU split kernel in bf16
     ("bf16", 64, 1, 12, 1, 4, 16, 16, [33], 25, 64),             # G = 12
+    ("bf16", 128, 2, 8, 2, 100, 40, 128, [150, 399], 110, 8),    # g = 100 > w: appends at 199 and 499
 ]
 
 
