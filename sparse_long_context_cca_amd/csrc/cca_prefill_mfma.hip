@@ -19,7 +19,9 @@
 //   * Workgroups are issued longest-first (the last positions see the most
 //     cores) and, when the kv heads divide evenly over the 8 XCDs, all
 //     workgroups of one kv head run on one XCD so that its core K/V stay in
-//     that XCD's L2.
+//     that XCD's L2.  An XCD that holds several kv heads runs them one after
+//     another (each longest-first), so the cores being read at any time are
+//     those of one head.
 // Per 64-key tile and wave
 //   S^T (64 keys x 32 rows) = K_tile . Q^T with v_mfma_f32_32x32x16_bf16
 //   (A = K rows from LDS, B = the wave's Q fragments, held in registers);
@@ -102,15 +104,17 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int j = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- which rows: longest first, XCD-aware
+  // ---- which rows: longest first, XCD-aware.  Block ids are dealt round
+  // robin over the XCDs; on XCD x the slots walk unit x*per's position blocks
+  // from the last down, then unit x*per+1's, and so on.
   const long bid = blockIdx.x;
   int pb, u;
   if (P.xcd) {
     const int per = P.U / 8;
     const long slot = bid >> 3;
     const int x = (int)(bid & 7);
-    pb = P.nPB - 1 - (int)(slot / per);
-    u = x * per + (int)(slot % per);
+    pb = P.nPB - 1 - (int)(slot % P.nPB);
+    u = x * per + (int)(slot / P.nPB);
   } else {
     pb = P.nPB - 1 - (int)(bid / P.U);
     u = (int)(bid % P.U);
