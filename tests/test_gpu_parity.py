@@ -178,6 +178,8 @@ PREFILL_CASES = [
     (1, 32, 2, 1500, 128, 16, 300),   # G = 16: two head groups of 8 per kv head
     (1, 12, 1, 900, 64, 16, 128),     # G = 12: head groups of 4
     (1, 4, 2, 1300, 128, 100, 150),   # g = 100
+    (1, 16, 16, 700, 64, 16, 64),     # 16 kv heads: two per XCD, run one after the other
+    (2, 32, 16, 600, 128, 16, 128),   # 32 (batch, kv head) units: four per XCD across the batch
 ]
 
 
