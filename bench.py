@@ -4,14 +4,18 @@
 A step is one pass of the prefill hot path over the LLaMA-3.1-8B GQA workload
 (batch 1, 32 query / 8 kv heads, head dim 128, L = 131072, g = 16, w = 1024,
 bf16): cca_pool_core then cca_attn_prefill, inputs already resident in HBM.
-The backward pass over the same workload (cca_attn_backward) and the decode
-workload (batch 8, 32/8 heads, 65536 cached tokens, 256 single-token steps) are
-timed in the same run and reported under "backward" and "decode"; a large bf16
-GEMM and a device-to-device copy give measured ceilings ("reference_rates")
-next to the spec peaks.
+In the same run, under "prefill_configs": the other prefill workloads (tiny
+fp32 L = 1024; LLaMA-2-7B MHA at 32K; LLaMA-2-7B MHA at 128K with spiky keys)
+and the headline one again, each as pool + prefill steps timed with events;
+under "backward": the backward pass over the headline workload; under
+"decode": the decode workload (batch 8, 32/8 heads, 65536 cached tokens, 256
+single-token steps).  A large bf16 GEMM, a device-to-device copy and a
+read-only reduction give measured ceilings ("reference_rates") next to the
+spec peaks.
 
 Prints ONE JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
---warmup W, --no-cpu (skip the CPU-oracle baseline), --no-decode, --no-backward.
+--warmup W, --no-cpu (skip the CPU-oracle baseline), --no-decode, --no-backward,
+--no-configs (skip the other prefill workloads).
 """
 from __future__ import annotations
 
@@ -32,6 +36,7 @@ import cca_inputs  # noqa: E402
 
 METRIC = "CCA prefill tokens/s + MFMA util at 128K (8B GQA shape, 1 GPU); decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_VALU_TFLOPS = 157.3  # MI355X fp32 vector peak (the fp32 prefill runs on the vector ALUs)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 
 
@@ -171,6 +176,63 @@ def cpu_oracle_baseline(cfg, q, k, v, budget_s=20.0):
     }
 
 
+def bench_prefill(cca, cfg, steps, warmup, inputs=None):
+    """Pool + prefill steps over one prefill workload (inputs resident on the
+    GPU), timed with events on the launch stream: the whole step and the
+    prefill launch alone.  Returns the per-config record and the device
+    tensors (so the caller can reuse them)."""
+    dev = "cuda:0"
+    if inputs is None:
+        q, k, v = cca_inputs.prefill_inputs(cfg)
+        inputs = (q.to(dev), k.to(dev), v.to(dev))
+    qd, kd, vd = inputs
+    m = cfg.L // cfg.g
+    ck = torch.empty((cfg.B, cfg.Hkv, max(m, 1), cfg.d), dtype=cca.core_dtype(qd.dtype), device=dev)
+    cv = torch.empty_like(ck)
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        cca.cca_pool_core(qd, kd, vd, ck, cv, cfg.g)
+        if ev is not None:
+            ev[0].record(stream)
+        cca.cca_attn_prefill(qd, kd, vd, ck, cv, out, cfg.g, cfg.w)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    prefill_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = total_ms / steps
+    prefill_avg = sum(prefill_ms) / len(prefill_ms)
+    pool_ms = ms_step - prefill_avg
+    assert torch.isfinite(out[0, :, -4:].float()).all()
+    flops = prefill_flops(cfg)
+    tflops = flops / (prefill_avg * 1e-3) / 1e12
+    bf16 = cfg.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_VALU_TFLOPS
+    rec = {
+        "workload": cfg.name, "dtype": cfg.dtype, "batch": cfg.B, "q_heads": cfg.Hq, "kv_heads": cfg.Hkv,
+        "seq_len": cfg.L, "head_dim": cfg.d, "group": cfg.g, "window": cfg.w, "steps": steps,
+        "ms_per_step": ms_step, "tokens_per_s": cfg.B * cfg.L / (ms_step * 1e-3),
+        "prefill_ms": prefill_avg, "pool_ms": pool_ms,
+        "algorithmic_flops": flops, "achieved_TFLOP_per_s": tflops,
+        "bound": "mfma" if bf16 else "alu", "peak": peak, "frac": tflops / peak,
+        "kernel": "prefill_mfma_kernel" if bf16 else "prefill_valu_kernel",
+        "pool_GB_per_s": pool_bytes(cfg) / (pool_ms * 1e-3) / 1e9 if pool_ms > 0 else None,
+    }
+    return rec, (qd, kd, vd), (ck, cv, out)
+
+
 def bench_backward(cca, cfg, qd, kd, vd, steps=2, warmup=1):
     """Backward pass over the prefill workload: forward with row statistics,
     then cca_attn_backward timed with events over `steps` calls.  Algorithmic
@@ -183,7 +245,7 @@ def bench_backward(cca, cfg, qd, kd, vd, steps=2, warmup=1):
     gen = torch.Generator(device=dev).manual_seed(4242)
     dout = torch.randn((B, Hq, L, d), generator=gen, device=dev).to(torch.bfloat16)
     m = L // g
-    ck = torch.empty((B, Hkv, m, d), dtype=torch.bfloat16, device=dev)
+    ck = torch.empty((B, Hkv, m, d), dtype=cca.core_dtype(qd.dtype), device=dev)
     cv = torch.empty_like(ck)
     out = torch.empty_like(qd)
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=dev)
@@ -192,7 +254,8 @@ def bench_backward(cca, cfg, qd, kd, vd, steps=2, warmup=1):
     dq = torch.empty((B, Hq, L, d), dtype=torch.float32, device=dev)
     dk = torch.empty((B, Hkv, L, d), dtype=torch.float32, device=dev)
     dv = torch.empty_like(dk)
-    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g), dtype=torch.uint8, device=dev)
+    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g, qd.dtype), dtype=torch.uint8,
+                     device=dev)
     for _ in range(warmup):
         cca.cca_attn_backward(qd, kd, vd, ck, cv, out, lse, dout, dq, dk, dv, ws, g, w)
     torch.cuda.synchronize()
@@ -213,19 +276,25 @@ def bench_backward(cca, cfg, qd, kd, vd, steps=2, warmup=1):
             "frac": tflops / PEAK_BF16_TFLOPS, "executed_mfma_flops": 14.0 * d * pairs,
             "mfma_busy": {k: measured_mfma_busy("backward_mfma_gqa_L131072", f"{k}_mfma_busy_fraction")
                           for k in ("dq", "dkv")},
-            "note": "bf16 matrix-core kernels (fp32 accumulate); gradients fp32"}
+            "note": "matrix-core kernels: bf16 operands for raw keys, fp16 for the cores (fp32 accumulate); "
+                    "gradients fp32"}
 
 
-def reference_rates(dev="cuda:0", n=16384, copy_bytes=1 << 30, reps=10):
-    """Measured ceilings on this GPU next to the spec peaks: a large dense bf16
-    GEMM through torch (hipBLASLt) and a device-to-device copy, each timed with
-    events over `reps` runs after one warm-up."""
+def reference_rates(dev="cuda:0", n=16384, copy_bytes=1 << 30, read_bytes=1 << 31, reps=10):
+    """Measured ceilings on this GPU next to the spec peaks, each timed with
+    events over `reps` runs after one warm-up: a large dense bf16 GEMM through
+    torch (hipBLASLt), a device-to-device copy (read + write), and a read-only
+    stream (torch's sum over a fp32 buffer, which reads every byte once and
+    writes one value) -- the ceiling for kernels that only read, like decode."""
     a = torch.randn((n, n), device=dev).to(torch.bfloat16)
     b = torch.randn((n, n), device=dev).to(torch.bfloat16)
     c = a @ b
     src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
+    rd = torch.ones(read_bytes // 4, dtype=torch.float32, device=dev)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
+    torch.sum(rd, dim=0, out=acc)
     torch.cuda.synchronize()
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     e[0].record()
@@ -235,14 +304,20 @@ def reference_rates(dev="cuda:0", n=16384, copy_bytes=1 << 30, reps=10):
     for _ in range(reps):
         dst.copy_(src)
     e[2].record()
+    for _ in range(reps):
+        torch.sum(rd, dim=0, out=acc)
+    e[3].record()
     torch.cuda.synchronize()
     gemm_ms = e[0].elapsed_time(e[1]) / reps
     copy_ms = e[1].elapsed_time(e[2]) / reps
-    del a, b, c, src, dst
+    read_ms = e[2].elapsed_time(e[3]) / reps
+    del a, b, c, src, dst, rd, acc
     torch.cuda.empty_cache()
     return {"bf16_gemm_TFLOP_per_s": 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12, "gemm_shape": f"{n}x{n}x{n}",
             "d2d_copy_GB_per_s": 2.0 * copy_bytes / (copy_ms * 1e-3) / 1e9,
-            "copy_bytes": copy_bytes, "copy_note": "read + write bytes per copy"}
+            "copy_bytes": copy_bytes, "copy_note": "read + write bytes per copy",
+            "read_only_GB_per_s": read_bytes / (read_ms * 1e-3) / 1e9, "read_bytes": read_bytes,
+            "read_note": "torch.sum over a fp32 buffer: bytes read per pass"}
 
 
 def bench_decode(cca, cfg, steps_timed=True):
@@ -254,7 +329,7 @@ def bench_decode(cca, cfg, steps_timed=True):
     kd, vd = x["k"].to(dev), x["v"].to(dev)
     qfull = torch.zeros((B, Hq, L, d), dtype=torch.bfloat16, device=dev)
     qfull[:, :, g - 1::g] = x["q_ends"].to(dev)
-    ck = torch.zeros((B, Hkv, m_cap, d), dtype=torch.bfloat16, device=dev)
+    ck = torch.zeros((B, Hkv, m_cap, d), dtype=cca.core_dtype(torch.bfloat16), device=dev)
     cv = torch.zeros_like(ck)
     cca.cca_pool_core(qfull, kd[:, :, :L].contiguous(), vd[:, :, :L].contiguous(), ck, cv, g)
     del qfull
@@ -338,6 +413,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="first run one device-to-device copy of this many bytes (a counter "
                          "calibration reference for FETCH_SIZE/WRITE_SIZE)")
@@ -360,45 +436,11 @@ def main():
     cfg = cca_inputs.CONFIGS[4]
     print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
     q, k, v = cca_inputs.prefill_inputs(cfg)
-    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    m = cfg.L // cfg.g
-    ck = torch.empty((cfg.B, cfg.Hkv, m, cfg.d), dtype=torch.bfloat16, device=dev)
-    cv = torch.empty_like(ck)
-    out = torch.empty_like(qd)
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        cca.cca_pool_core(qd, kd, vd, ck, cv, cfg.g)
-        if ev is not None:
-            ev[0].record(stream)
-        cca.cca_attn_prefill(qd, kd, vd, ck, cv, out, cfg.g, cfg.w)
-        if ev is not None:
-            ev[1].record(stream)
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    prefill_ms = [a.elapsed_time(b) for a, b in evs]
-    ms_step = total_ms / args.steps
-    prefill_avg = sum(prefill_ms) / len(prefill_ms)
-    pool_ms = ms_step - prefill_avg
-    assert torch.isfinite(out[0, :, -4:].float()).all()
-
-    flops = prefill_flops(cfg)
-    tflops = flops / (prefill_avg * 1e-3) / 1e12
+    print(f"[bench] {cfg.name}: warmup {args.warmup}, timing {args.steps} steps", file=sys.stderr, flush=True)
+    head, (qd, kd, vd), (ck, cv, out) = bench_prefill(cca, cfg, args.steps, args.warmup,
+                                                      (q.to(dev), k.to(dev), v.to(dev)))
+    ms_step, prefill_avg, pool_ms = head["ms_per_step"], head["prefill_ms"], head["pool_ms"]
+    flops, tflops = head["algorithmic_flops"], head["achieved_TFLOP_per_s"]
     tokens = cfg.B * cfg.L
     result = {
         "metric": METRIC,
@@ -437,8 +479,22 @@ def main():
     if not args.no_backward:
         print("[bench] backward", file=sys.stderr, flush=True)
         result["backward"] = bench_backward(cca, cfg, qd, kd, vd)
+    if not args.no_configs:
+        # every prefill workload, the headline one included, in one list
+        recs = []
+        qd = kd = vd = None
+        torch.cuda.empty_cache()
+        for number in (1, 2, 3):
+            c = cca_inputs.CONFIGS[number]
+            print(f"[bench] prefill workload {c.name}", file=sys.stderr, flush=True)
+            rec, dev_in, dev_out = bench_prefill(cca, c, steps=10 if number > 1 else 20, warmup=3)
+            recs.append(rec)
+            del dev_in, dev_out
+            torch.cuda.empty_cache()
+        recs.append(head)
+        result["prefill_configs"] = recs
     if not args.no_decode:
-        del qd, kd, vd
+        qd = kd = vd = None
         torch.cuda.empty_cache()
         print("[bench] decode", file=sys.stderr, flush=True)
         result["decode"] = bench_decode(cca, cca_inputs.CONFIGS[5])
@@ -452,6 +508,7 @@ def main():
         result["pool"]["frac_of_measured_copy"] = result["pool"]["GB_per_s"] / ref["d2d_copy_GB_per_s"]
     if "decode" in result:
         result["decode"]["frac_of_measured_copy"] = result["decode"]["GB_per_s"] / ref["d2d_copy_GB_per_s"]
+        result["decode"]["frac_of_measured_read"] = result["decode"]["GB_per_s"] / ref["read_only_GB_per_s"]
     if not args.no_cpu:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_oracle_baseline(cfg, q, k, v)

@@ -77,7 +77,7 @@ def attention_block(x, wqkv, wo, spec, g, w, cos, sin, cca, events=None):
     k = apply_rope(k, cos, sin).contiguous()
     rec()
     m = L // g
-    ck = torch.empty((1, Hkv, max(m, 1), d), dtype=x.dtype, device=x.device)
+    ck = torch.empty((1, Hkv, max(m, 1), d), dtype=cca.core_dtype(x.dtype), device=x.device)
     cv = torch.empty_like(ck)
     o = torch.empty((1, Hq, L, d), dtype=x.dtype, device=x.device)
     cca.cca_pool_core(q, k, v, ck, cv, g)

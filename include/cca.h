@@ -36,14 +36,23 @@
  *   - Arguments are validated on the host before anything is enqueued; on an
  *     error nothing is enqueued and a status other than CCA_OK is returned,
  *     with a message available from cca_last_error() (per thread).
- *   - Input dtype `dt` applies to q, k, v and the core/ring caches.
+ *   - Input dtype `dt` applies to q, k, v, the new token and the decode ring.
  *     Supported: d in {64, 128}; dt in {CCA_F32, CCA_BF16}; out_dt in
  *     {dt, CCA_F32}.  Every buffer must hold at most 2^40 elements (offsets are
  *     64-bit); sequence lengths, g, w, the ring size R and m_cap are below
  *     2^30 (positions are 32-bit).  Beyond either: CCA_ERR_UNSUPPORTED.
+ *   - Core cache dtype: cca_core_dtype(dt), i.e. fp32 cores for fp32 inputs
+ *     and FP16 cores for bf16 inputs (same element size as the inputs).  A
+ *     core is a weighted mean of its group's keys (values); with keys of
+ *     magnitude ~15 the bf16 rounding of the cores alone moves attention
+ *     outputs by ~0.03, fp16 rounding by ~0.003.  For bf16 inputs the products
+ *     with cores therefore run on fp16 operands: q (and in the backward dout)
+ *     is converted to fp16 for them, so q, k, v and dout must stay below
+ *     fp16's range limit (|x| < 65504); beyond it results are undefined.
  *   - Rounding: accumulation is fp32; core K/V and outputs are rounded to their
  *     storage dtype once, to nearest even.  bf16 attention feeds the matrix
- *     cores bf16 operands (probabilities are rounded to bf16 before P*V).
+ *     cores bf16 operands for raw keys and fp16 operands for cores; the
+ *     probabilities are rounded to that operand type before P*V.
  */
 #ifndef CCA_H
 #define CCA_H
@@ -63,7 +72,9 @@ typedef enum cca_status {
   CCA_ERR_HIP = 4          /* a HIP launch failed; see cca_last_error() */
 } cca_status;
 
-typedef enum cca_dtype { CCA_F32 = 0, CCA_BF16 = 1 } cca_dtype;
+/* Element types.  CCA_F16 names the core cache of bf16 inputs only; it is not
+ * accepted as an input or output dtype. */
+typedef enum cca_dtype { CCA_F32 = 0, CCA_BF16 = 1, CCA_F16 = 2 } cca_dtype;
 
 /*
  * Pooling rule for the core token of a group (used by cca_pool_core_ex and
@@ -96,6 +107,10 @@ const char* cca_status_string(int status);
 /* Message of the last error returned on the calling thread ("" if none). */
 const char* cca_last_error(void);
 
+/* Dtype of the core cache (core_k, core_v) for input dtype dt: CCA_F32 for
+ * CCA_F32, CCA_F16 for CCA_BF16; -1 for any other value. */
+int cca_core_dtype(int dt);
+
 /*
  * cca_visibility_table - integer index tables of the visibility rule above.
  *   n_core[t] and win_lo[t] for t < L (int32 [L]); group_last[j] = (j+1)g-1
@@ -111,8 +126,8 @@ cca_status cca_visibility_table(int L, int g, int w, int32_t* n_core, int32_t* w
  *     qbar = mean over the G query heads of Q[b, h, (j+1)g-1, :]
  *     a    = softmax_tau(qbar . K[b, kv, jg+tau, :] / sqrt(d)), tau < g
  *     core_k[b, kv, j, :] = sum_tau a_tau K[b, kv, jg+tau, :]   (same for V)
- *   q [B,Hq,L,d], k/v [B,Hkv,L,d] (dt); core_k/core_v [B,Hkv,m_cap,d] (dt),
- *   slots j < m written, others untouched.  weights: NULL, or fp32
+ *   q [B,Hq,L,d], k/v [B,Hkv,L,d] (dt); core_k/core_v [B,Hkv,m_cap,d]
+ *   (cca_core_dtype(dt)), slots j < m written, others untouched.  weights: NULL, or fp32
  *   [B,Hkv,m,g] receiving a (for tests).
  * Errors: INVALID_ARG (null, L<1, g<1, B/Hq/Hkv<1), UNSUPPORTED (d, dt,
  *   Hq % Hkv), CAPACITY (m_cap < m).
@@ -175,17 +190,20 @@ cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, c
 
 /*
  * cca_attn_backward_workspace_bytes - device workspace cca_attn_backward needs
- *   (two fp32 row statistics per row, [B,Hq,L,2], and the core gradients
- *   2 x [B,Hkv,L/g,d] fp32); 0 for sizes below 1.
+ *   for input dtype dt: two fp32 row statistics per row, [B,Hq,L,2], the core
+ *   gradients 2 x [B,Hkv,L/g,d] fp32, and for bf16 inputs fp16 copies of q and
+ *   dout (2 x [B,Hq,L,d], from a 256-byte boundary), which the products with
+ *   the fp16 cores read; 0 for sizes below 1 or an unknown dt.
  */
-size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g);
+size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g,
+                                         cca_dtype dt);
 
 /*
  * cca_attn_backward - gradients of the whole forward (pooling with rule
  *   pool_mode, then the fused prefill) w.r.t. q, k and v, given the upstream
  *   gradient dout of out:
- *     q, k, v, core_k, core_v, out, dout in dt (out and dout [B,Hq,L,d]; out
- *     and the cores as the forward wrote them); lse fp32 [B,Hq,L] from
+ *     q, k, v, out, dout in dt, core_k, core_v in cca_core_dtype(dt) (out and
+ *     dout [B,Hq,L,d]; out and the cores as the forward wrote them); lse fp32 [B,Hq,L] from
  *     cca_attn_prefill_train; dq [B,Hq,L,d], dk, dv [B,Hkv,L,d] fp32, fully
  *     overwritten.  Per row: dS = P (dP - dout . out); dq, and the raw and
  *     core key/value gradients, as in the chain rule; the core gradients then
@@ -260,7 +278,10 @@ cca_status cca_cache_fill_ring(const void* k, const void* v, void* ring_k, void*
 
 /*
  * cca_decode_workspace_bytes - size of the workspace cca_attn_decode needs for
- * these shapes (fp32 partial softmax states of its split-K pass).
+ * these shapes (fp32 partial softmax states of its split-K pass).  It takes
+ * Hkv and the core capacity m_cap rather than a maximal context length: the
+ * split plan depends on the longest visible range, m_cap + w, and on how many
+ * (b, kv head) pairs share the GPU.
  */
 size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int g, int w);
 
@@ -271,7 +292,8 @@ size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int 
  *   q_t [B,Hq,d], k_t/v_t [B,Hkv,d] (dt): the new token's projections.
  *   ring_k/ring_v [B,Hkv,R,d] (dt): raw keys/values, position p in slot p % R;
  *     must hold positions max(0, t-R+1) .. t-1.  R >= max(w, g).
- *   core_k/core_v [B,Hkv,m_cap,d] (dt): cores of every completed group.
+ *   core_k/core_v [B,Hkv,m_cap,d] (cca_core_dtype(dt)): cores of every
+ *     completed group.
  *   Enqueued work: (1) k_t/v_t are written to slot t % R; (2) when (t+1) % g
  *   == 0, group (t+1)/g-1 is pooled from positions t-g+1 .. t with the mean
  *   over its G heads of q_t and written to core slot (t+1)/g-1 (it is not yet
@@ -279,12 +301,14 @@ size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int 
  *   raw window win_lo(t) .. t (the same row prefill computes for position t).
  *   out: [B,Hq,d] in out_dt.  workspace: device memory of at least
  *   cca_decode_workspace_bytes(...) bytes, contents need no initialisation.
- *   pos: int32 [B] device array; read, and incremented by one after the step
- *   when advance_pos != 0 (so that a step can be replayed in a loop; it stays
- *   at INT32_MAX once there).
+ *   pos: int32 [B] device array; read, and, when advance_pos != 0,
+ *   incremented by one after a valid step, so that a loop of steps needs no
+ *   host work and can be captured in a graph.  With advance_pos = 0 pos is
+ *   read-only and the caller advances it.  (A read-only pos is the plain
+ *   form; the device-side advance is an addition for replayed loops.)
  *   A sequence with t < 0, t = INT32_MAX or floor((t+1)/g) > m_cap (no core
- *   slot left) gets NaN outputs and no cache writes (pos lives on the device,
- *   so this cannot be reported as a status).
+ *   slot left) gets NaN outputs, no cache writes and keeps its pos (pos lives
+ *   on the device, so this cannot be reported as a status).
  * Errors: INVALID_ARG, UNSUPPORTED as above; CAPACITY when R < max(w, g) or
  *   the workspace is too small.
  */

@@ -21,10 +21,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcca.so")
 
 CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_CAPACITY, CCA_ERR_HIP = range(5)
-CCA_F32, CCA_BF16 = 0, 1
+CCA_F32, CCA_BF16, CCA_F16 = 0, 1, 2
 CCA_POOL_SOFTMAX, CCA_POOL_SOFTMAX_HEADS, CCA_POOL_MEAN, CCA_POOL_MAX = range(4)
 
-EXPORTS = ["cca_version", "cca_status_string", "cca_last_error", "cca_visibility_table",
+EXPORTS = ["cca_version", "cca_status_string", "cca_last_error", "cca_core_dtype", "cca_visibility_table",
            "cca_pool_core", "cca_pool_core_ex", "cca_attn_prefill", "cca_attn_prefill_ex",
            "cca_decode_workspace_bytes", "cca_attn_decode", "cca_attn_decode_ex",
            "cca_pool_core_chunk", "cca_attn_prefill_chunk", "cca_cache_fill_ring",
@@ -54,6 +54,7 @@ def load() -> ctypes.CDLL:
         "cca_version": ([], I),
         "cca_status_string": ([I], ctypes.c_char_p),
         "cca_last_error": ([], ctypes.c_char_p),
+        "cca_core_dtype": ([I], I),
         "cca_visibility_table": ([I, I, I, P, P, P, P], I),
         "cca_pool_core": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, P], I),
         "cca_pool_core_ex": ([P, P, P, P, P, I, P, I, I, I, I, I, I, I, I, P], I),
@@ -66,7 +67,7 @@ def load() -> ctypes.CDLL:
         "cca_attn_prefill_chunk": ([P, P, P, P, P, I, P, I, P, P, I, I, I, I, I, I, I, I, I, P], I),
         "cca_cache_fill_ring": ([P, P, P, P, I, P, I, I, I, I, I, P], I),
         "cca_attn_prefill_train": ([P, P, P, P, P, I, P, I, P, I, I, I, I, I, I, I, I, P], I),
-        "cca_attn_backward_workspace_bytes": ([I, I, I, I, I, I], S),
+        "cca_attn_backward_workspace_bytes": ([I, I, I, I, I, I, I], S),
         "cca_attn_backward": ([P, P, P, P, P, I, P, P, P, P, P, P, P, S, I, I, I, I, I, I, I, I, I, P], I),
     }
     for name, (args, res) in sig.items():
@@ -103,6 +104,15 @@ def _ptr(t):
 
 
 _FLOAT = (torch.float32, torch.bfloat16)
+_TORCH_OF = {CCA_F32: torch.float32, CCA_BF16: torch.bfloat16, CCA_F16: torch.float16}
+
+
+def core_dtype(dtype: torch.dtype) -> torch.dtype:
+    """torch dtype of the core cache for inputs of ``dtype`` (cca_core_dtype: fp32 for fp32,
+    fp16 for bf16)."""
+    if dtype not in _FLOAT:
+        raise CCAError(CCA_ERR_UNSUPPORTED, f"dtype {dtype} not supported")
+    return _TORCH_OF[load().cca_core_dtype(CCA_F32 if dtype == torch.float32 else CCA_BF16)]
 
 
 def _expect(tensors) -> None:
@@ -165,7 +175,8 @@ def cca_visibility_table(L: int, g: int, w: int, n_core: torch.Tensor, win_lo: t
 
 def cca_pool_core(q, k, v, core_k, core_v, g: int, weights=None, mode: int = CCA_POOL_SOFTMAX,
                   stream=None) -> None:
-    """q [B,Hq,L,d]; k, v [B,Hkv,L,d]; core_k, core_v [B,Hkv,m_cap,d]; weights fp32 [B,Hkv,L//g,g];
+    """q [B,Hq,L,d]; k, v [B,Hkv,L,d]; core_k, core_v [B,Hkv,m_cap,d] in core_dtype(k.dtype);
+    weights fp32 [B,Hkv,L//g,g];
     mode: one of the CCA_POOL_* rules (q gives the shapes; the mean and max rules do not read it)."""
     B, Hq, L, d = _dims(q, 4, "q")
     Hkv = _dims(k, 4, "k")[1]
@@ -173,7 +184,8 @@ def cca_pool_core(q, k, v, core_k, core_v, g: int, weights=None, mode: int = CCA
     dt = (k.dtype,)
     spec = [("q", q, (B, Hq, L, d), dt), ("k", k, (B, Hkv, L, d), _FLOAT), ("v", v, (B, Hkv, L, d), dt)]
     if core_k is not None or core_v is not None:
-        spec += [("core_k", core_k, (B, Hkv, m_cap, d), dt), ("core_v", core_v, (B, Hkv, m_cap, d), dt)]
+        ct = (core_dtype(k.dtype),)
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), ct), ("core_v", core_v, (B, Hkv, m_cap, d), ct)]
     if weights is not None:
         spec.append(("weights", weights, (B, Hkv, L // g if g > 0 else 0, g), (torch.float32,)))
     _expect(spec)
@@ -198,7 +210,8 @@ def _attn_spec(q, k, v, core_k, core_v, out, B, Hq, Hkv, Lq, Lk, d, m_cap):
     spec = [("q", q, (B, Hq, Lq, d), _FLOAT), ("k", k, (B, Hkv, Lk, d), dt), ("v", v, (B, Hkv, Lk, d), dt),
             ("out", out, (B, Hq, Lq, d), (q.dtype, torch.float32))]
     if core_k is not None or core_v is not None:
-        spec += [("core_k", core_k, (B, Hkv, m_cap, d), dt), ("core_v", core_v, (B, Hkv, m_cap, d), dt)]
+        ct = (core_dtype(q.dtype),)
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), ct), ("core_v", core_v, (B, Hkv, m_cap, d), ct)]
     return spec
 
 
@@ -221,7 +234,8 @@ def cca_attn_decode(q_t, k_t, v_t, ring_k, ring_v, core_k, core_v, pos, out, wor
             ("ring_k", ring_k, (B, Hkv, R, d), dt), ("ring_v", ring_v, (B, Hkv, R, d), dt),
             ("pos", pos, (B,), (torch.int32,)), ("out", out, (B, Hq, d), (q_t.dtype, torch.float32))]
     if core_k is not None or core_v is not None:
-        spec += [("core_k", core_k, (B, Hkv, m_cap, d), dt), ("core_v", core_v, (B, Hkv, m_cap, d), dt)]
+        ct = (core_dtype(q_t.dtype),)
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), ct), ("core_v", core_v, (B, Hkv, m_cap, d), ct)]
     _expect(spec + _workspace("workspace", workspace))
     _check(load().cca_attn_decode_ex(_ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(ring_k), _ptr(ring_v), R,
                                      _ptr(core_k), _ptr(core_v), m_cap, _ptr(pos), int(advance_pos),
@@ -248,7 +262,8 @@ def cca_pool_core_chunk(q, k, v, core_k, core_v, g: int, q_start, q_len,
     spec = [("q", q, (B, Hq, Lq, d), dt), ("k", k, (B, Hkv, Lk, d), _FLOAT), ("v", v, (B, Hkv, Lk, d), dt),
             ("q_start", q_start, (B,), (torch.int32,)), ("q_len", q_len, (B,), (torch.int32,))]
     if core_k is not None or core_v is not None:
-        spec += [("core_k", core_k, (B, Hkv, m_cap, d), dt), ("core_v", core_v, (B, Hkv, m_cap, d), dt)]
+        ct = (core_dtype(k.dtype),)
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), ct), ("core_v", core_v, (B, Hkv, m_cap, d), ct)]
     _expect(spec)
     _check(load().cca_pool_core_chunk(_ptr(q), _ptr(k), _ptr(v), _ptr(core_k), _ptr(core_v), m_cap,
                                       _rows(q_start), _rows(q_len), B, Hq, Hkv, Lq, Lk, d, g, _dt(k),
@@ -294,8 +309,12 @@ def cca_attn_prefill_train(q, k, v, core_k, core_v, out, lse, g: int, w: int, st
                                          _stream(stream)))
 
 
-def cca_attn_backward_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, d: int, g: int) -> int:
-    return int(load().cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g))
+def cca_attn_backward_workspace_bytes(B: int, Hq: int, Hkv: int, L: int, d: int, g: int,
+                                      dtype: torch.dtype = torch.bfloat16) -> int:
+    """Workspace bytes of cca_attn_backward for inputs of ``dtype`` (bf16 also holds fp16
+    copies of q and dout)."""
+    dt = CCA_F32 if dtype == torch.float32 else CCA_BF16
+    return int(load().cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g, dt))
 
 
 def cca_attn_backward(q, k, v, core_k, core_v, out, lse, dout, dq, dk, dv, workspace, g: int, w: int,

@@ -86,7 +86,13 @@ cca_status check_sizes(const char* fn, long long a, long long b, long long c) {
 
 extern "C" {
 
-int cca_version(void) { return 100; }
+int cca_version(void) { return 20000; }
+
+int cca_core_dtype(int dt) {
+  if (dt == CCA_F32) return CCA_F32;
+  if (dt == CCA_BF16) return CCA_F16;
+  return -1;
+}
 
 const char* cca_status_string(int status) {
   switch (status) {
@@ -304,9 +310,10 @@ cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, c
       cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, lse, dt, s), fn);
 }
 
-size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g) {
+size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g, cca_dtype dt) {
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || d < 1 || g < 1) return 0;
-  return cca::backward_workspace_bytes(B, Hq, Hkv, L, d, g);
+  if (dt != CCA_F32 && dt != CCA_BF16) return 0;
+  return cca::backward_workspace_bytes(B, Hq, Hkv, L, d, g, dt);
 }
 
 cca_status cca_attn_backward(const void* q, const void* k, const void* v, const void* core_k,
@@ -343,7 +350,7 @@ cca_status cca_attn_backward(const void* q, const void* k, const void* v, const 
   if (st != CCA_OK) return st;
   if ((long long)B * Hkv > 65535 || (long long)Hq > 65535)
     return fail(CCA_ERR_UNSUPPORTED, "%s: B*Hkv or Hq exceeds 65535", fn);
-  const size_t need = cca::backward_workspace_bytes(B, Hq, Hkv, L, d, g);
+  const size_t need = cca::backward_workspace_bytes(B, Hq, Hkv, L, d, g, dt);
   if (workspace_bytes < need)
     return fail(CCA_ERR_CAPACITY, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes, need);
   REQUIRE_PTR(workspace);

@@ -567,6 +567,14 @@ __global__ __launch_bounds__(256) void pool_backward_kernel(
   }
 }
 
+// Workspace: row statistics (2 floats per row), dCK, dCV (fp32), then for
+// bf16 inputs, from a 256-byte boundary, fp16 copies of q and dO.
+size_t f32_part_bytes(const Shape& sh) {
+  const size_t m = sh.g > 0 ? (size_t)(sh.L / sh.g) : 0;
+  return (2 * (size_t)sh.B * sh.Hq * sh.L + 2 * (size_t)sh.B * sh.Hkv * m * sh.d) * sizeof(float);
+}
+size_t f16_copies_offset(const Shape& sh) { return (f32_part_bytes(sh) + 255) & ~(size_t)255; }
+
 template <int DT, int D>
 hipError_t launch_backward_t(const void* q, const void* k, const void* v, const void* ck,
                              const void* cv, int m_cap, const void* out, const float* lse,
@@ -584,10 +592,12 @@ hipError_t launch_backward_t(const void* q, const void* k, const void* v, const 
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)std::min<long>((nws + 255) / 256, 4096)), dim3(256),
                        0, s, dck, nws);
   }
-  if (DT == 1) {
+  if constexpr (DT == 1) {
     // bf16: matrix-core kernels (cca_backward_mfma.hip)
+    uint16_t* q16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(ws) + f16_copies_offset(sh));
+    uint16_t* do16 = q16 + (size_t)rows * D;
     const hipError_t e = launch_backward_mfma(q, k, v, ck, cv, m_cap, out, lse, dout, dq, dk, dv,
-                                              reinterpret_cast<float2*>(ws), dck, dcv, sh, s);
+                                              reinterpret_cast<float2*>(ws), dck, dcv, q16, do16, sh, s);
     if (e != hipSuccess) return e;
   } else {
     float* Dv = ws;
@@ -632,9 +642,10 @@ hipError_t launch_backward_t(const void* q, const void* k, const void* v, const 
 
 }  // namespace
 
-size_t backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g) {
-  const size_t m = g > 0 ? (size_t)(L / g) : 0;
-  return (2 * (size_t)B * Hq * L + 2 * (size_t)B * Hkv * m * d) * sizeof(float);
+size_t backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g, int dt) {
+  const Shape sh{B, Hq, Hkv, L, d, g, 1};
+  if (dt == 0) return f32_part_bytes(sh);
+  return f16_copies_offset(sh) + 2 * (size_t)B * Hq * L * d * sizeof(uint16_t);
 }
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* ck,

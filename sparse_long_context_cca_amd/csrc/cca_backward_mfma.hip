@@ -1,5 +1,6 @@
 // Backward pass of the CCA attention prefill on the gfx950 matrix cores (bf16
-// operands, fp32 accumulate and gradients).
+// operands for the raw keys, fp16 for the cores, which are stored in fp16;
+// fp32 accumulate and gradients).
 //
 // Gradients of the fused softmax (digest at digest.lyk-ai.com/posts/2412.12465,
 // "Method", fusion formula; the pages fine-tune with CCA attention in place:
@@ -11,7 +12,8 @@
 //   dq_t = sum_k dS key_k / sqrt(d)                      (dq_mfma_kernel)
 //   dkey_k = sum_t dS q_t / sqrt(d), dvalue_k = sum_t P dO_t   (dkv_mfma_kernel)
 // Kernels, in launch order:
-//   1. row_stats_kernel  per row {lse * log2(e), D_t}
+//   1. row_stats_kernel  per row {lse * log2(e), D_t}, and fp16 copies of q
+//                        and dO for the core products
 //   2. dq_mfma_kernel    row-parallel, the forward's work decomposition: per
 //                        64-key tile S^T = K.Q^T and dP^T = V.dO^T (K, V rows
 //                        from LDS, Q and dO fragments in registers), and
@@ -49,22 +51,41 @@ constexpr int kCoreSplit = 8192;   // rows per core unit (absolute, aligned spli
 
 // ------------------------------------------------------------- 1. statistics
 
-// stats[row] = {lse[row] * log2(e), dO_row . O_row}; 16 lanes per row.
+// stats[row] = {lse[row] * log2(e), dO_row . O_row}; 16 lanes per row.  The
+// pass also writes fp16 copies of the row's q and dO (q16, do16): the core
+// products of the dK/dV kernel take their Q and dO tiles from them, since the
+// cores they meet are fp16.
 template <int D>
 __global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* __restrict__ out,
                                                         const uint16_t* __restrict__ dout,
+                                                        const uint16_t* __restrict__ q,
                                                         const float* __restrict__ lse,
-                                                        float2* __restrict__ stats, long rows) {
-  constexpr int LPR = 16, EPL = D / LPR;
+                                                        float2* __restrict__ stats,
+                                                        uint16_t* __restrict__ q16,
+                                                        uint16_t* __restrict__ do16, long rows) {
+  constexpr int LPR = 16, EPL = D / LPR, NW = EPL / 2;  // NW dwords (bf16 pairs) per lane
+  typedef uint32_t words __attribute__((ext_vector_type(NW)));
   const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPR;
   const int part = threadIdx.x % LPR;
   const bool valid = row < rows;
   float acc = 0.f;
   if (valid) {
-    const uint16_t* o = out + row * D + part * EPL;
-    const uint16_t* gg = dout + row * D + part * EPL;
+    const long off = row * D + part * EPL;
+    const words o = *reinterpret_cast<const words*>(out + off);
+    const words gg = *reinterpret_cast<const words*>(dout + off);
+    const words qq = *reinterpret_cast<const words*>(q + off);
+    words q16w, g16w;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc = fmaf(bf16_to_f32(o[e]), bf16_to_f32(gg[e]), acc);
+    for (int i = 0; i < NW; ++i) {
+      const float o0 = __uint_as_float(o[i] << 16), o1 = __uint_as_float(o[i] & 0xffff0000u);
+      const float g0 = __uint_as_float(gg[i] << 16), g1 = __uint_as_float(gg[i] & 0xffff0000u);
+      acc = fmaf(o0, g0, acc);
+      acc = fmaf(o1, g1, acc);
+      g16w[i] = pack_f16x2(g0, g1);
+      q16w[i] = pack_f16x2(__uint_as_float(qq[i] << 16), __uint_as_float(qq[i] & 0xffff0000u));
+    }
+    *reinterpret_cast<words*>(q16 + off) = q16w;
+    *reinterpret_cast<words*>(do16 + off) = g16w;
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -133,14 +154,14 @@ void dq_mfma_kernel(DqParams P) {
   const int P_hi = min(L - 1, P_lo + P.RP - 1);
   const int t_raw = row0 + j;
   const int t = min(t_raw, L - 1);
-  const int my_nc = n_core(t, g, w), my_lo = win_lo(t, w);
   const int w_lo = uni(min(row0, L - 1)), w_hi = uni(min(row0 + 31, L - 1));
   const int wnc_lo = uni(n_core(w_lo, g, w));
   const int wlo_hi = uni(win_lo(w_hi, w));
+  // key tiles: raw tiles 0 .. n_rt-1 (bf16 operands), then core tiles (fp16)
   const int nc_hi = uni(n_core(P_hi, g, w));
-  const int n_ct = (nc_hi + kTileRows - 1) / kTileRows;
+  const int n_ct = uni((nc_hi + kTileRows - 1) / kTileRows);
   const int r0 = win_lo(P_lo, w) & ~(kTileRows - 1);
-  const int n_rt = (P_hi - r0) / kTileRows + 1;
+  const int n_rt = uni((P_hi - r0) / kTileRows + 1);
   const int n_tiles = uni(n_ct + n_rt);
 
   const uint16_t* kbase = P.k + (long)kvp * L * D;
@@ -175,8 +196,8 @@ void dq_mfma_kernel(DqParams P) {
       soff[i] = chunk < CPR ? (row * D + 8 * chunk) * 2 : 0x40000000;
     }
   }
-  auto tile_core = [&](int it) { return it < n_ct; };
-  auto tile_base = [&](int it) { return it < n_ct ? it * kTileRows : r0 + (it - n_ct) * kTileRows; };
+  auto tile_core = [&](int it) { return it >= n_rt; };
+  auto tile_base = [&](int it) { return it >= n_rt ? (it - n_rt) * kTileRows : r0 + it * kTileRows; };
   auto kbuf = [&](int s) { return lds + s * KT::kBytes; };
   auto vbuf = [&](int s) { return lds + 4 * KT::kBytes + s * VBytes; };
   auto load_tile = [&](int kslot, int vslot, int it) {
@@ -207,9 +228,9 @@ void dq_mfma_kernel(DqParams P) {
   const int s16 = lane & 15;
   const int ktr_off = hh * KT::kGroup + (s16 >> 2) * KT::kRow + 2 * (16 * ((lane >> 4) & 1) + 4 * (s16 & 3));
 
-  auto tile_full = [&](int it) {
+  auto tile_full = [&](int it, bool core) {
     const int base = tile_base(it);
-    return tile_core(it) ? base + kTileRows <= wnc_lo : (base >= wlo_hi && base + kTileRows - 1 <= w_lo);
+    return core ? base + kTileRows <= wnc_lo : (base >= wlo_hi && base + kTileRows - 1 <= w_lo);
   };
 
   f32x16 dqt[DB];
@@ -219,12 +240,13 @@ void dq_mfma_kernel(DqParams P) {
     for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
   const float c = P.c;
   // dQ^T += K^T . dS^T for chunk cc (16 keys) and dim block db of a tile
-  auto dq_mfma = [&](const char* kt, int cc, int db, const bf16x8& dsf) {
+  // (F16: a core tile)
+  auto dq_mfma = [&](const char* kt, int cc, int db, const bf16x8& dsf, auto core_tag) {
     const char* p0 = kt + ktr_off + (4 * cc) * KT::kGroup + 64 * db;
     const bf16x4 x0 = lds_read_tr16(p0);
     const bf16x4 x1 = lds_read_tr16(p0 + 2 * KT::kGroup);
     const bf16x8 a = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-    dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf, dqt[db], 0, 0, 0);
+    dqt[db] = mfma32<decltype(core_tag)::value>(a, dsf, dqt[db]);
   };
 
   // prologue: tiles 0 and 1; K slot 3 (read as "tile -1" with dS = 0) cleared
@@ -244,9 +266,13 @@ void dq_mfma_kernel(DqParams P) {
   // computes S^T and dP^T of tile it, then runs the dQ product of tile it-1
   // interleaved with tile it's P and dS (the forward's P.V / exponential
   // interleave): chunk cc of dsb is consumed by the product just before tile
-  // it's chunk cc overwrites it.
+  // it's chunk cc overwrites it.  CUR and PREV say whether tiles it and it-1
+  // are core tiles (fp16 operands) or raw tiles (bf16).
   int kslot = 0, vslot = 0;
-  for (int it = 0; it < n_tiles; ++it) {
+  // key_lo .. key_hi: the keys of this phase (raw positions, or cores) that
+  // this lane's row sees
+  auto iteration = [&](int it, auto cur_tag, auto prev_tag, int key_lo, int key_hi) {
+    constexpr bool CUR = decltype(cur_tag)::value;
     const int kprev = (kslot + 3) & 3;
     load_tile((kslot + 2) & 3, vslot == 0 ? 2 : vslot - 1, it + 2);
     const char* kt = kbuf(kslot);
@@ -262,18 +288,17 @@ void dq_mfma_kernel(DqParams P) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + krow_off + kb * 8 * KT::kGroup + 32 * ks);
-        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sx[kb], 0, 0, 0);
+        sx[kb] = mfma32<CUR>(a, qf[ks], sx[kb]);
         const bf16x8 av = *reinterpret_cast<const bf16x8*>(vt + vrow_off + kb * 32 * VRow + 32 * ks);
-        dpx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gf[ks], dpx[kb], 0, 0, 0);
+        dpx[kb] = mfma32<CUR>(av, gf[ks], dpx[kb]);
       }
-    if (!tile_full(it)) {
+    if (!tile_full(it, CUR)) {
       // key kk = 32kb + 8(r/4) + 4hh + r%4 of the tile is visible to this
       // lane's row iff lo_rel <= kk <= hi_rel; hidden keys get P = 0
       asm volatile("" ::: "memory");  // keeps this a real (scalar) branch
       const int base = tile_base(it);
-      const bool core = tile_core(it);
-      const int lo_rel = core ? 0 : my_lo - base;
-      const int hi_rel = core ? my_nc - 1 - base : t - base;
+      const int lo_rel = key_lo - base;
+      const int hi_rel = key_hi - base;
       const unsigned span = (unsigned)(hi_rel - lo_rel);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -290,32 +315,52 @@ void dq_mfma_kernel(DqParams P) {
     constexpr int PPM = 32 / NDQ;   // scores per MFMA slot
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      bf16x8 dnew;
+      u32x4 dnew;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dq_mfma(kt_prev, cc, db, dsb[cc]);
+        dq_mfma(kt_prev, cc, db, dsb[cc], prev_tag);
 #pragma unroll
-        for (int e = db * PPM; e < db * PPM + PPM; ++e) {
+        for (int e = db * PPM; e < db * PPM + PPM; e += 2) {
           const int r = (cc & 1) * 8 + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r], c, -lse2));
-          dnew[e] = static_cast<__bf16>(p * (dpx[cc >> 1][r] - Dt));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r], c, -lse2));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r + 1], c, -lse2));
+          dnew[e >> 1] = pack_op<CUR>(p0 * (dpx[cc >> 1][r] - Dt), p1 * (dpx[cc >> 1][r + 1] - Dt));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      dsb[cc] = dnew;
+      dsb[cc] = __builtin_bit_cast(bf16x8, dnew);
     }
     kslot = (kslot + 1) & 3;
     vslot = vslot == 2 ? 0 : vslot + 1;
     sync_stage();
+  };
+  // raw tiles on bf16 Q and dO fragments, then the core tiles on fp16 ones
+  // (the conversion is one-way: no fp16 value is converted back; the other
+  // order's round trip spilled registers inside this kernel's loops)
+  {
+    const int my_lo = win_lo(t, w);
+    for (int it = 0; it < n_rt; ++it) iteration(it, RawTile{}, RawTile{}, my_lo, t);
+  }
+  if (n_ct > 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = bf16_frag_to_f16(qf[ks]);
+      gf[ks] = bf16_frag_to_f16(gf[ks]);
+    }
+    const int my_nc = n_core(t, g, w);
+    iteration(n_rt, CoreTile{}, RawTile{}, 0, my_nc - 1);
+    for (int it = n_rt + 1; it < n_tiles; ++it) iteration(it, CoreTile{}, CoreTile{}, 0, my_nc - 1);
   }
   // dQ of the last tile (K slot (n_tiles-1)%4)
-  {
+  auto last_tile = [&](auto core_tag) {
     const char* kt_last = kbuf((kslot + 3) & 3);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dq_mfma(kt_last, cc, db, dsb[cc]);
-  }
+      for (int db = 0; db < DB; ++db) dq_mfma(kt_last, cc, db, dsb[cc], core_tag);
+  };
+  if (n_ct > 0) last_tile(CoreTile{});
+  else last_tile(RawTile{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
@@ -342,6 +387,8 @@ struct DkvParams {
   const uint16_t* ck;
   const uint16_t* cv;
   const uint16_t* dout;
+  const uint16_t* q16;   // fp16 copies of q and dout (row_stats_kernel), read by core units
+  const uint16_t* do16;
   const float2* stats;
   float* dk;   // raw-key gradients [B,Hkv,L,d]
   float* dv;
@@ -396,7 +443,12 @@ void dkv_mfma_kernel(DkvParams P) {
     u = (int)(bid / BH);
   }
   const int b = kvp / P.Hkv;
-  const bool core = u < P.nCB * P.nSplit;
+  // core units meet fp16 cores: every product runs on fp16 operands, with Q
+  // and dO from their fp16 copies; raw units run on bf16 operands
+  auto unit = [&](auto core_tag) {
+  constexpr bool core = decltype(core_tag)::value;
+  const uint16_t* qsrc = core ? P.q16 : P.q;
+  const uint16_t* gsrc = core ? P.do16 : P.dout;
   int key_lo, key_lim, t_lo, t_end;
   if (core) {
     const int split = u / P.nCB, cb = u % P.nCB;
@@ -471,8 +523,8 @@ void dkv_mfma_kernel(DkvParams P) {
     const int t0 = t_lo + tile * kTileRows;
     const int nr = it < n_it ? max(0, min(kTileRows, t_end + 1 - t0)) : 0;
     const long row = ((long)b * P.Hq + (long)(kvp % P.Hkv) * P.G + hg) * L + t0;
-    const u32x4 rq = buffer_desc(P.q + row * D, nr * D * 2);
-    const u32x4 rg = buffer_desc(P.dout + row * D, nr * D * 2);
+    const u32x4 rq = buffer_desc(qsrc + row * D, nr * D * 2);
+    const u32x4 rg = buffer_desc(gsrc + row * D, nr * D * 2);
     const u32x4 rs = buffer_desc(P.stats + row, nr * 8);
     const uint32_t qa = lds_addr(qbuf(slot)), ga = lds_addr(gbuf(slot)), sa = lds_addr(sbuf(slot));
     // load li = wave + NW i: which array it fills is uniform (a scalar select).
@@ -532,14 +584,15 @@ void dkv_mfma_kernel(DkvParams P) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(qt + rrow_off + 32 * ks);
-      sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sx, 0, 0, 0);
+      sx = mfma32<core>(a, kf[ks], sx);
       const bf16x8 ag = *reinterpret_cast<const bf16x8*>(gt + rrow_off + 32 * ks);
       const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vfrag + 1024 * ks);
-      dpx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vf, dpx, 0, 0, 0);
+      dpx = mfma32<core>(ag, vf, dpx);
     }
-    // P and dS (bf16 fragments of k-steps 2 half and 2 half + 1)
+    // P and dS (fragments of k-steps 2 half and 2 half + 1, in the unit's
+    // operand type)
     const bool full = wave_keys_ok && tw >= lo_max && tw + 31 <= hi_min;
-    bf16x8 pb[2], dsb[2];
+    u32x4 pw[2], dsw[2];
     auto probs = [&](auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
       const unsigned span = (unsigned)(hi - lo);
@@ -550,16 +603,21 @@ void dkv_mfma_kernel(DkvParams P) {
         const float4 s23 = *reinterpret_cast<const float4*>(sta + rr * 8 + 16);
         const float l2[4] = {s01.x, s01.z, s23.x, s23.z};
         const float dd[4] = {s01.y, s01.w, s23.y, s23.w};
+        float p[4], ds[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int r = 4 * q4 + x;
-          float p = __builtin_amdgcn_exp2f(fmaf(sx[r], c, -l2[x]));
+          p[x] = __builtin_amdgcn_exp2f(fmaf(sx[r], c, -l2[x]));
           if (MASK) {
             const bool vis = hi >= lo && (unsigned)(t0 + rr + x - lo) <= span;
-            p = vis ? p : 0.f;
+            p[x] = vis ? p[x] : 0.f;
           }
-          pb[q4 >> 1][4 * (q4 & 1) + x] = static_cast<__bf16>(p);
-          dsb[q4 >> 1][4 * (q4 & 1) + x] = static_cast<__bf16>(p * (dpx[r] - dd[x]));
+          ds[x] = p[x] * (dpx[r] - dd[x]);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; x += 2) {
+          pw[q4 >> 1][2 * (q4 & 1) + x / 2] = pack_op<core>(p[x], p[x + 1]);
+          dsw[q4 >> 1][2 * (q4 & 1) + x / 2] = pack_op<core>(ds[x], ds[x + 1]);
         }
       }
     };
@@ -574,10 +632,10 @@ void dkv_mfma_kernel(DkvParams P) {
         const int o = rtr_off + (4 * cc) * RT::kGroup + 64 * db;
         const bf16x4 g0 = lds_read_tr16(gt + o), g1 = lds_read_tr16(gt + o + 2 * RT::kGroup);
         const bf16x8 ag = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
-        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, pb[h2], dvt[db], 0, 0, 0);
+        dvt[db] = mfma32<core>(ag, __builtin_bit_cast(bf16x8, pw[h2]), dvt[db]);
         const bf16x4 q0 = lds_read_tr16(qt + o), q1 = lds_read_tr16(qt + o + 2 * RT::kGroup);
         const bf16x8 aq = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[h2], dkt[db], 0, 0, 0);
+        dkt[db] = mfma32<core>(aq, __builtin_bit_cast(bf16x8, dsw[h2]), dkt[db]);
       }
     }
     slot = slot == 2 ? 0 : slot + 1;
@@ -617,7 +675,7 @@ void dkv_mfma_kernel(DkvParams P) {
     }
 
   // lane holds dims 32db + 8(r/4) + 4hh + r%4 of its key
-  if (!core) {
+  if constexpr (!core) {
     const long orow = ((long)kvp * L + key) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -641,6 +699,9 @@ void dkv_mfma_kernel(DkvParams P) {
         atomicAdd(P.dcv + orow + d, dvt[db][r]);
       }
   }
+  };
+  if (u < P.nCB * P.nSplit) unit(CoreTile{});
+  else unit(RawTile{});
 }
 
 constexpr int kDqWaves = 8;
@@ -657,14 +718,15 @@ int gcd_int(int a, int b) {
 template <int D>
 hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck, const void* cv,
                     int m_cap, const void* out, const float* lse, const void* dout, float* dq,
-                    float* dk, float* dv, float2* stats, float* dck, float* dcv, const Shape& sh,
-                    hipStream_t s) {
+                    float* dk, float* dv, float2* stats, float* dck, float* dcv, uint16_t* q16,
+                    uint16_t* do16, const Shape& sh, hipStream_t s) {
   const int B = sh.B, Hq = sh.Hq, Hkv = sh.Hkv, L = sh.L, g = sh.g, w = sh.w;
   const int m = L / g;
   const float scale = 1.0f / sqrtf((float)D), c = kLog2e * scale;
   const long rows = (long)B * Hq * L;
   hipLaunchKernelGGL((row_stats_kernel<D>), dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, stats, rows);
+                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout),
+                     static_cast<const uint16_t*>(q), lse, stats, q16, do16, rows);
 
   DqParams Q;
   Q.q = static_cast<const uint16_t*>(q);
@@ -702,6 +764,8 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck,
   K.ck = Q.ck;
   K.cv = Q.cv;
   K.dout = Q.dout;
+  K.q16 = q16;
+  K.do16 = do16;
   K.stats = stats;
   K.dk = dk;
   K.dv = dv;
@@ -734,10 +798,11 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck,
 hipError_t launch_backward_mfma(const void* q, const void* k, const void* v, const void* ck,
                                 const void* cv, int m_cap, const void* out, const float* lse,
                                 const void* dout, float* dq, float* dk, float* dv, float2* stats,
-                                float* dck, float* dcv, const Shape& sh, hipStream_t s) {
+                                float* dck, float* dcv, uint16_t* q16, uint16_t* do16,
+                                const Shape& sh, hipStream_t s) {
   if (sh.d == 64)
-    return launch_t<64>(q, k, v, ck, cv, m_cap, out, lse, dout, dq, dk, dv, stats, dck, dcv, sh, s);
-  return launch_t<128>(q, k, v, ck, cv, m_cap, out, lse, dout, dq, dk, dv, stats, dck, dcv, sh, s);
+    return launch_t<64>(q, k, v, ck, cv, m_cap, out, lse, dout, dq, dk, dv, stats, dck, dcv, q16, do16, sh, s);
+  return launch_t<128>(q, k, v, ck, cv, m_cap, out, lse, dout, dq, dk, dv, stats, dck, dcv, q16, do16, sh, s);
 }
 
 }  // namespace cca

@@ -18,6 +18,7 @@
 //   optionally advances pos[b].
 // HBM-bound: every visible K/V byte is read once per step.
 #include <algorithm>
+#include <type_traits>
 
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
@@ -73,9 +74,9 @@ __device__ __forceinline__ void pool_new_group(int mode, const char* q_t, const 
       break;
   }
   const int lane = threadIdx.x & 63;
-  if (lane < RL::LPK) {
-    Row16<DT>::store(ck + lane * RL::EPL * RL::ES, acck);
-    Row16<DT>::store(cv + lane * RL::EPL * RL::ES, accv);
+  if (lane < RL::LPK) {  // the core dtype has the input's element size
+    Row16<core_dt(DT)>::store(ck + lane * RL::EPL * RL::ES, acck);
+    Row16<core_dt(DT)>::store(cv + lane * RL::EPL * RL::ES, accv);
   }
 }
 
@@ -171,9 +172,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       const char* kr = nullptr;
       const char* vr = nullptr;
       if (ok[j]) {
-        if (f < nc) {
-          kr = ck + (long)f * D * ES;
-          vr = cv + (long)f * D * ES;
+        if (f < nc) {  // cores: the core dtype, same element size
+          Slice<core_dt(DT)>::load(ck + ((long)f * D + d0) * ES, kx[j]);
+          Slice<core_dt(DT)>::load(cv + ((long)f * D + d0) * ES, vx[j]);
         } else {
           const int p = lo + (f - nc);
           if (p == t) {
@@ -183,9 +184,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
             kr = ring_k + (long)(p % R) * D * ES;
             vr = ring_v + (long)(p % R) * D * ES;
           }
+          S::load(kr + d0 * ES, kx[j]);
+          S::load(vr + d0 * ES, vx[j]);
         }
-        S::load(kr + d0 * ES, kx[j]);
-        S::load(vr + d0 * ES, vx[j]);
       } else {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) kx[j][e] = vx[j][e] = 0.f;
@@ -277,12 +278,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
 }
 
-// Pass 1 on the matrix cores (bf16, G <= 8 query heads per kv head).
+// Pass 1 on the matrix cores (bf16 inputs, G <= 8 query heads per kv head).
 // grid = (splits, 1, B * Hkv); four waves per block.  Each wave streams its own
-// 32-key tiles of the block's key range -- no block barrier in the main loop:
-//   S^T (32 keys x 32 columns) = K . Q^T with v_mfma_f32_32x32x16_bf16; the
-//   columns are the kv head's G query heads, the rest zero (the matrix cores
-//   have ample headroom here: the loop is bound by HBM);
+// 32-key tiles of the block's key range -- no block barrier in the main loop.
+// The block's raw keys come first (bf16 operands), then its cores (fp16, the
+// core cache's dtype; the Q fragments are converted once in registers), so no
+// tile mixes the two:
+//   S^T (32 keys x 32 columns) = K . Q^T with v_mfma_f32_32x32x16_{bf16,f16};
+//   the columns are the kv head's G query heads, the rest zero (the matrix
+//   cores have ample headroom here: the loop is bound by HBM);
 //   K rows go straight from memory into the A operand registers;
 //   V rows are transposed through a wave-private LDS tile into V^T, with the
 //   key order permuted to match the score layout, so P^T is used in place as
@@ -299,6 +303,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
     const int32_t* __restrict__ pos, float* __restrict__ ws_m, float* __restrict__ ws_l,
     float* __restrict__ ws_o, int Hq, int Hkv, int g, int w, int splits, float c, int pool_mode) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   typedef float f32x16 __attribute__((ext_vector_type(16)));
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   constexpr int KS = D / 16;            // k-steps of K.Q^T
@@ -385,98 +390,128 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m = -INFINITY, l = 0.f;
   char* vt = lds + wave * VBytes;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  for (int f0 = f_begin + wave * kDecBK; f0 < f_end; f0 += 4 * kDecBK) {
-    // K rows -> A operand registers (zero past f_end)
-    u32x4 ka[KS];
-    {
-      const int f = f0 + j;
-      const bool ok = f < f_end;
-      const uint16_t* kr = ok ? krow(f, false) : k_new;
+  // The wave's tiles of keys fb .. fe-1, all raw (CORE false: bf16) or all
+  // cores (CORE true: fp16).
+  auto run = [&](int fb, int fe, auto core_tag) {
+    constexpr bool CORE = decltype(core_tag)::value;
+    auto mfma = [](const bf16x8& a, const bf16x8& bq, const f32x16& acc) {
+      if constexpr (CORE)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, bq), acc, 0, 0, 0);
+      else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc, 0, 0, 0);
+    };
+    for (int f0 = fb + wave * kDecBK; f0 < fe; f0 += 4 * kDecBK) {
+      // K rows -> A operand registers (zero past fe)
+      u32x4 ka[KS];
+      {
+        const int f = f0 + j;
+        const bool ok = f < fe;
+        const uint16_t* kr = ok ? krow(f, false) : k_new;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ka[ks] = ok ? *reinterpret_cast<const u32x4*>(kr + 16 * ks + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // V rows: lane covers NVP (key quad, dim octet) pairs
-    u32x4 va[NVP][4];
-#pragma unroll
-    for (int pi = 0; pi < NVP; ++pi) {
-      const int pair = lane + 64 * pi;
-      const int q = pair % (kDecBK / 4), oct = pair / (kDecBK / 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = f0 + 4 * q + i;
-        va[pi][i] = f < f_end ? *reinterpret_cast<const u32x4*>(krow(f, true) + 8 * oct)
-                              : u32x4{0u, 0u, 0u, 0u};
+        for (int ks = 0; ks < KS; ++ks)
+          ka[ks] = ok ? *reinterpret_cast<const u32x4*>(kr + 16 * ks + 8 * hh) : u32x4{0u, 0u, 0u, 0u};
       }
-    }
-    // S^T = K.Q^T
-    f32x16 sx;
+      // V rows: lane covers NVP (key quad, dim octet) pairs
+      u32x4 va[NVP][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sx[r] = 0.f;
+      for (int pi = 0; pi < NVP; ++pi) {
+        const int pair = lane + 64 * pi;
+        const int q = pair % (kDecBK / 4), oct = pair / (kDecBK / 4);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[ks]), qb[ks], sx, 0, 0, 0);
-    // V^T into the wave's LDS tile (keys permuted: bits 2 and 3 swapped)
-#pragma unroll
-    for (int pi = 0; pi < NVP; ++pi) {
-      const int pair = lane + 64 * pi;
-      const int q = pair % (kDecBK / 4), oct = pair / (kDecBK / 4);
-      const int k0 = 4 * q;
-      const int kpos0 = (k0 & ~15) | ((k0 & 4) << 1) | ((k0 & 8) >> 1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int dw = i >> 1;
-        const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t lo2 = __builtin_amdgcn_perm(va[pi][1][dw], va[pi][0][dw], sel);
-        const uint32_t hi2 = __builtin_amdgcn_perm(va[pi][3][dw], va[pi][2][dw], sel);
-        *reinterpret_cast<uint2*>(vt + (8 * oct + i) * kDecVRow + 2 * kpos0) = make_uint2(lo2, hi2);
+        for (int i = 0; i < 4; ++i) {
+          const int f = f0 + 4 * q + i;
+          va[pi][i] = f < fe ? *reinterpret_cast<const u32x4*>(krow(f, true) + 8 * oct)
+                             : u32x4{0u, 0u, 0u, 0u};
+        }
       }
-    }
-    // mask keys past the range; key of register r = 8(r/4) + 4hh + r%4
-    if (f0 + kDecBK > f_end) {
+      // S^T = K.Q^T
+      f32x16 sx;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 8 * (r >> 2) + 4 * hh + (r & 3);
-        sx[r] = f0 + kk < f_end ? sx[r] : -INFINITY;
+      for (int r = 0; r < 16; ++r) sx[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sx = mfma(__builtin_bit_cast(bf16x8, ka[ks]), qb[ks], sx);
+      // V^T into the wave's LDS tile (keys permuted: bits 2 and 3 swapped)
+#pragma unroll
+      for (int pi = 0; pi < NVP; ++pi) {
+        const int pair = lane + 64 * pi;
+        const int q = pair % (kDecBK / 4), oct = pair / (kDecBK / 4);
+        const int k0 = 4 * q;
+        const int kpos0 = (k0 & ~15) | ((k0 & 4) << 1) | ((k0 & 8) >> 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int dw = i >> 1;
+          const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t lo2 = __builtin_amdgcn_perm(va[pi][1][dw], va[pi][0][dw], sel);
+          const uint32_t hi2 = __builtin_amdgcn_perm(va[pi][3][dw], va[pi][2][dw], sel);
+          *reinterpret_cast<uint2*>(vt + (8 * oct + i) * kDecVRow + 2 * kpos0) = make_uint2(lo2, hi2);
+        }
       }
-    }
-    float mt = -INFINITY;
+      // mask keys past the range; key of register r = 8(r/4) + 4hh + r%4
+      if (f0 + kDecBK > fe) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sx[r]);
-    {
-      auto rr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(rr[0]), __uint_as_float(rr[1]));
-    }
-    const float mnew = fmaxf(m, mt);
-    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
-    m = mnew;
-    l *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    const float mc = (m == -INFINITY ? 0.f : m) * c;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      bf16x2 pk;
-      pk[0] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sx[r], c, -mc)));
-      pk[1] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sx[r + 1], c, -mc)));
-      l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l, false);
-      pb[r >> 3][r & 7] = pk[0];
-      pb[r >> 3][(r & 7) + 1] = pk[1];
-    }
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + j) * kDecVRow + (16 * cc + 8 * hh) * 2);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cc], o[db], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 8 * (r >> 2) + 4 * hh + (r & 3);
+          sx[r] = f0 + kk < fe ? sx[r] : -INFINITY;
+        }
       }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sx[r]);
+      {
+        auto rr = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(rr[0]), __uint_as_float(rr[1]));
+      }
+      const float mnew = fmaxf(m, mt);
+      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      const float mc = (m == -INFINITY ? 0.f : m) * c;
+      // probabilities rounded to the tile's operand type; the row sum adds
+      // exactly the rounded values the P.V product uses
+      u32x4 pw[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sx[r], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sx[r + 1], c, -mc));
+        uint32_t pk;
+        if constexpr (CORE) {
+          typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+          pk = pack_f16x2(p0, p1);
+          l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), f16x2{(_Float16)1.0f, (_Float16)1.0f}, l, false);
+        } else {
+          typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+          pk = pack_bf16x2(p0, p1);
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                              bf16x2{static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)}, l, false);
+        }
+        pw[r >> 3][(r & 7) >> 1] = pk;
+      }
+      // O^T += V^T . P^T
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (32 * db + j) * kDecVRow + (16 * cc + 8 * hh) * 2);
+          o[db] = mfma(a, __builtin_bit_cast(bf16x8, pw[cc]), o[db]);
+        }
+    }
+  };
+  // raw keys of this split (bf16), then its cores (fp16)
+  run(max(f_begin, nc), f_end, std::false_type{});
+  if (f_begin < nc) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f16x8 h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(static_cast<float>(qb[ks][e]));
+      qb[ks] = __builtin_bit_cast(bf16x8, h);
+    }
+    run(f_begin, min(f_end, nc), std::true_type{});
   }
 
   // merge the four waves: lane (column j, half hh) holds dims 32db + 8(r/4) + 4hh + r%4
@@ -522,7 +557,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
 }
 
 // Pass 2.  One block of D threads per (b, query head).  The split states are
-// staged in LDS first so that the weighted sum issues independent loads.
+// staged in LDS first so that the weighted sum issues independent loads.  A
+// valid step never has t = INT32_MAX (decode_valid), so the advance of pos
+// cannot overflow.
 constexpr int kMaxSplits = 128;
 
 template <int OT, int D>
@@ -569,9 +606,12 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
     lsum = fmaf(sl[s], f, lsum);
     osum = fmaf(ws_o[(st0 + s) * D + e], f, osum);
   }
-  const float r = red[1] != 0.f ? NAN : osum / lsum;
+  // an invalid step (every split marked NaN: validity depends on t alone)
+  // writes NaN and leaves pos where it is
+  const bool invalid = red[1] != 0.f;
+  const float r = invalid ? NAN : osum / lsum;
   EO::store(static_cast<typename EO::T*>(out_), bh * D + e, r);
-  if (advance_pos && e == 0 && bh % Hq == 0 && pos[bh / Hq] < 0x7fffffff) pos[bh / Hq] += 1;
+  if (advance_pos && e == 0 && bh % Hq == 0 && !invalid) pos[bh / Hq] += 1;
 }
 
 int pick_gt(int G) {

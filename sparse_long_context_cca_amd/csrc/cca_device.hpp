@@ -68,7 +68,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Element access by dtype (0 = fp32, 1 = bf16).
+// fp16 <-> fp32 (the core cache of bf16 inputs).  Widening is exact;
+// narrowing rounds to nearest even.
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+// Two floats -> packed fp16x2 in one dword (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 f2 __attribute__((ext_vector_type(2)));
+  f2 v;
+  v[0] = static_cast<_Float16>(a);
+  v[1] = static_cast<_Float16>(b);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Storage dtype of the core cache for input dtype DT: fp32 cores for fp32
+// inputs, fp16 cores for bf16 inputs.  A core is a convex combination of the
+// group's keys (values), so it needs their range but more precision than bf16
+// gives: with keys of magnitude ~15 the bf16 rounding of the cores alone moves
+// attention outputs by ~0.03, the fp16 rounding by ~0.003.
+constexpr int core_dt(int dt) { return dt == 0 ? 0 : 2; }
+
+// Element access by dtype (0 = fp32, 1 = bf16, 2 = fp16).
 template <int DT>
 struct Elem;
 template <>
@@ -82,6 +106,12 @@ struct Elem<1> {
   typedef bf16_bits T;
   static __device__ __forceinline__ float load(const T* p, long i) { return bf16_to_f32(p[i]); }
   static __device__ __forceinline__ void store(T* p, long i, float x) { p[i] = f32_to_bf16(x); }
+};
+template <>
+struct Elem<2> {
+  typedef uint16_t T;
+  static __device__ __forceinline__ float load(const T* p, long i) { return f16_to_f32(p[i]); }
+  static __device__ __forceinline__ void store(T* p, long i, float x) { p[i] = f32_to_f16(x); }
 };
 
 // Wave64 reductions.

@@ -61,21 +61,24 @@ hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void
                          const Shape& sh, int dt, int pool_mode, hipStream_t s);
 
 // Backward pass (cca_backward.hip).  Workspace: two fp32 row statistics per
-// row [B,Hq,L,2] and the core gradients dCK, dCV [B,Hkv,L/g,d] (fp32).
-size_t backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g);
+// row [B,Hq,L,2], the core gradients dCK, dCV [B,Hkv,L/g,d] (fp32), and for
+// bf16 inputs (from a 256-byte boundary) fp16 copies of q and dO [B,Hq,L,d].
+size_t backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g, int dt);
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* ck,
                            const void* cv, int m_cap, const void* out, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, void* ws,
                            const Shape& sh, int dt, int pool_mode, hipStream_t s);
 
 // bf16 matrix-core part of the backward (cca_backward_mfma.hip): row
-// statistics {lse log2(e), dO.O} into stats [B,Hq,L], dq (fully written), the
-// raw-key dk, dv (fully written) and the core gradients added into dck, dcv
-// ([B,Hkv,L/g,d], zeroed by the caller).
+// statistics {lse log2(e), dO.O} into stats [B,Hq,L] and fp16 copies of q and
+// dO into q16, do16 [B,Hq,L,d], dq (fully written), the raw-key dk, dv (fully
+// written) and the core gradients added into dck, dcv ([B,Hkv,L/g,d], zeroed
+// by the caller).
 hipError_t launch_backward_mfma(const void* q, const void* k, const void* v, const void* ck,
                                 const void* cv, int m_cap, const void* out, const float* lse,
                                 const void* dout, float* dq, float* dk, float* dv, float2* stats,
-                                float* dck, float* dcv, const Shape& sh, hipStream_t s);
+                                float* dck, float* dcv, uint16_t* q16, uint16_t* do16,
+                                const Shape& sh, hipStream_t s);
 
 // Copies positions max(0, len-R) .. len-1 of sequence b's K and V (len =
 // seq_len[b], device) into ring slot p % R; a len outside 0 .. Lk copies nothing.

@@ -11,6 +11,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
+#include "cca_device.hpp"
+
 namespace cca {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -18,6 +22,53 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---- typed matrix-core operations on 16-bit operands
+// Fragments are held as bf16x8 whatever their type: bf16 for the raw keys and
+// values (the inputs' dtype), fp16 (the same bits reinterpreted) for the
+// cores, which are stored in fp16.  F16 selects the instruction.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef std::integral_constant<bool, true> CoreTile;   // fp16 operands
+typedef std::integral_constant<bool, false> RawTile;   // bf16 operands
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Two values rounded (nearest even) to the operand type, packed in a dword.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_op(float a, float b) {
+  if constexpr (F16) return pack_f16x2(a, b);
+  else return pack_bf16x2(a, b);
+}
+// bf16 fragment -> fp16 fragment (exact for 2^-17 <= |x| < 65504; a
+// smaller bf16 value is rounded to fp16's subnormal grid of 2^-24).
+__device__ __forceinline__ bf16x8 bf16_frag_to_f16(const bf16x8& x) {
+  f16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(static_cast<float>(x[e]));
+  return __builtin_bit_cast(bf16x8, h);
+}
+// The way back, fp16 fragment -> bf16 fragment: exact for a fragment that
+// came from bf16_frag_to_f16, except for the values below 2^-17 that it
+// rounded, which stay within 2^-25 of the original.
+__device__ __forceinline__ bf16x8 f16_frag_to_bf16(const bf16x8& x) {
+  const f16x8 h = __builtin_bit_cast(f16x8, x);
+  bf16x8 b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = static_cast<__bf16>(static_cast<float>(h[e]));
+  return b;
+}
 
 // 32-bit LDS address of a pointer into a __shared__ array.  (Address-space
 // casts live in plain functions: inside a kernel template they have no host

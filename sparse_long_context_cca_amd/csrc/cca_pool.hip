@@ -13,7 +13,8 @@
 // One wave64 per group.  Each lane owns a 16-byte slice of one key row, so a
 // wave load covers 1 KB of the group's contiguous K (or V) rows and every byte
 // of K and V is read exactly once (twice for K in the per-head mode).
-// HBM-bound: reads K, V and the G query rows at group ends, writes CK and CV.
+// HBM-bound: reads K, V and the G query rows at group ends, writes CK and CV
+// (fp16 for bf16 inputs, fp32 for fp32 inputs; rounded once, to nearest even).
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
 #include "cca_pool_group.hpp"
@@ -79,10 +80,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ q_,
   float acck[RL::EPL], accv[RL::EPL];
   float* wout = weights != nullptr ? weights + ((long)bh * m + j) * g : nullptr;
   pool_group<DT, D, MODE>(krow, vrow, qrow, g, G, scale_log2, acck, accv, wout);
-  if (lane < RL::LPK) {
+  if (lane < RL::LPK) {  // cores in the core dtype (same element size as the input)
     const long crow = ((long)bh * m_cap + j) * D + lane * RL::EPL;
-    Row16<DT>::store(static_cast<char*>(ck_) + crow * RL::ES, acck);
-    Row16<DT>::store(static_cast<char*>(cv_) + crow * RL::ES, accv);
+    Row16<core_dt(DT)>::store(static_cast<char*>(ck_) + crow * RL::ES, acck);
+    Row16<core_dt(DT)>::store(static_cast<char*>(cv_) + crow * RL::ES, accv);
   }
 }
 

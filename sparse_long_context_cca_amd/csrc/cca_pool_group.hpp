@@ -63,6 +63,28 @@ struct Row16<1> {
   }
 };
 
+template <>
+struct Row16<2> {  // fp16 (the core cache of bf16 inputs)
+  static constexpr int N = 8;
+  static __device__ __forceinline__ void load(const void* p, float* x) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = f16_to_f32((uint16_t)(w[i] & 0xffffu));
+      x[2 * i + 1] = f16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  }
+  static __device__ __forceinline__ void store(void* p, const float* x) {
+    uint4 v;
+    v.x = pack_f16x2(x[0], x[1]);
+    v.y = pack_f16x2(x[2], x[3]);
+    v.z = pack_f16x2(x[4], x[5]);
+    v.w = pack_f16x2(x[6], x[7]);
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+};
+
 template <int DT, int D>
 struct RowLanes {
   static constexpr int ES = DT == 0 ? 4 : 2;   // element bytes

@@ -1,4 +1,4 @@
-// Fused CCA prefill on the gfx950 matrix cores (bf16 operands, fp32 accumulate).
+// Fused CCA prefill on the gfx950 matrix cores (bf16 raw and fp16 core operands, fp32 accumulate).
 //
 // Row t of head h computes one softmax over [cores 0..n_core(t) ; raw keys
 // win_lo(t)..t] (digest at digest.lyk-ai.com/posts/2412.12465, "Method",
@@ -13,9 +13,16 @@
 //     in LDS serves all eight waves.
 //   * The workgroup walks the union of its rows' visible keys: first the core
 //     tiles 0..n_core(last row) (64 cores each), then the raw tiles covering
-//     win_lo(first row)..last row (64 positions each, 64-aligned).  Tiles that
-//     every row of a wave sees completely skip the mask; tiles no row of a
-//     wave sees are skipped by that wave.
+//     win_lo(first row)..last row (64 positions each, 64-aligned).  Tiles
+//     that every row of a wave sees completely skip the mask; tiles no row of
+//     a wave sees are fully masked.
+//   * The cores are stored in fp16 (three more mantissa bits than bf16: a
+//     core is a weighted mean of keys that can be large), so core tiles run
+//     on fp16 MFMAs with the Q fragments converted to fp16 in registers and
+//     the probabilities rounded to fp16; raw tiles run on bf16 MFMAs (the
+//     inputs' dtype) with Q converted back (the round trip returns every
+//     |q| >= 2^-17 exactly, smaller ones within 2^-25).  Cores first: in a
+//     same-process comparison the other order ran 2% slower.
 //   * Workgroups are issued longest-first (the last positions see the most
 //     cores) and, when the kv heads divide evenly over the 8 XCDs, all
 //     workgroups of one kv head run on one XCD so that its core K/V stay in
@@ -23,14 +30,14 @@
 //     another (each longest-first), so the cores being read at any time are
 //     those of one head.
 // Per 64-key tile and wave
-//   S^T (64 keys x 32 rows) = K_tile . Q^T with v_mfma_f32_32x32x16_bf16
+//   S^T (64 keys x 32 rows) = K_tile . Q^T with v_mfma_f32_32x32x16_{bf16,f16}
 //   (A = K rows from LDS, B = the wave's Q fragments, held in registers);
 //   each lane then holds 32 scores of one query row, so the row max needs one
 //   exchange with lane l^32.  The row sum of the rounded probabilities is
 //   taken on the matrix cores too: one 16x16x32 MFMA per P chunk whose A
 //   operand selects, for output rows 0 and 1, the lanes that hold query rows
 //   0..15 and 16..31 (the sum does not depend on the key order).
-//   P (bf16) is used in place as the B operand of O^T += V^T . P^T; the V^T
+//   P (bf16 or fp16) is used in place as the B operand of O^T += V^T . P^T; the V^T
 //   operand comes from a row-major V tile through transposing LDS reads that
 //   follow the key order of the score layout.  The P.V product of tile i-1
 //   is interleaved with the exponentials of tile i, so the matrix cores work
@@ -158,12 +165,12 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int wnc_lo = uni(n_core(w_lo, g, w));
   const int wlo_hi = uni(win_lo(w_hi, w));
 
-  // ---- workgroup key range
+  // ---- workgroup key range: core tiles 0 .. n_ct-1, then raw tiles
   const int nc_hi = uni(n_core(P_hi, g, w));
-  const int n_ct = (nc_hi + kBK - 1) / kBK;
+  const int n_ct = uni((nc_hi + kBK - 1) / kBK);
   const int raw_lo = win_lo(P_lo, w);
   const int r0 = raw_lo & ~(kBK - 1);
-  const int n_rt = (P_hi - r0) / kBK + 1;
+  const int n_rt = uni((P_hi - r0) / kBK + 1);
   const int n_tiles = uni(n_ct + n_rt);
 
   const long kvrow = (long)kvp;
@@ -253,9 +260,9 @@ void prefill_mfma_kernel(PrefillParams P) {
   };
   // Does tile it need a mask for this wave's rows?  (wave-uniform)  A tile
   // none of the wave's rows can see is simply fully masked.
-  auto tile_full = [&](int it) {
+  auto tile_full = [&](int it, bool core) {
     const int base = tile_base(it);
-    return tile_core(it) ? base + kBK <= wnc_lo : (base >= wlo_hi && base + kBK - 1 <= w_lo);
+    return core ? base + kBK <= wnc_lo : (base >= wlo_hi && base + kBK - 1 <= w_lo);
   };
 
   f32x16 o[DB];
@@ -271,13 +278,19 @@ void prefill_mfma_kernel(PrefillParams P) {
   // c+16 and c+48 (query row c+16).  Lane c < 16 holds C[0][c] and C[1][c]
   // in lsum[0] and lsum[1]; the other rows of C stay zero.
   f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 sel;
+  // the selector in both operand types (the transition tile sums a raw tile's
+  // bf16 probabilities while its own are fp16)
+  const bool sel_on = lane == 0 || lane == 32 || lane == 17 || lane == 49;
+  bf16x8 sel_bf, sel_h;
   {
-    const bool on = lane == 0 || lane == 32 || lane == 17 || lane == 49;
+    f16x8 s16;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sel[e] = static_cast<__bf16>(on ? 1.0f : 0.0f);
+    for (int e = 0; e < 8; ++e) {
+      sel_bf[e] = static_cast<__bf16>(sel_on ? 1.0f : 0.0f);
+      s16[e] = static_cast<_Float16>(sel_on ? 1.0f : 0.0f);
+    }
+    sel_h = __builtin_bit_cast(bf16x8, s16);
   }
-  auto row_sum_mfma = [&](const bf16x8& p) { lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, p, lsum, 0, 0, 0); };
   // rescale the row sums by their rows' factors (lane c < 16 needs those of
   // rows c and c+16, held by lanes c and c+16)
   auto rescale_sums = [&](float a) {
@@ -286,7 +299,6 @@ void prefill_mfma_kernel(PrefillParams P) {
     lsum[1] *= a_hi;
   };
   const float c = P.c;
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
   // End of a pipeline stage: this wave's loads of the previous stage (K(it+1),
   // V(it)) have landed in LDS, then the workgroup meets.  Loads finish in
@@ -314,7 +326,9 @@ void prefill_mfma_kernel(PrefillParams P) {
 
   // Iteration it: LDS holds K(it) (K slot it%3) and V(it-1) (V slot
   // (it+2)%3); K(it+1) and V(it) are landing.  It issues the loads of K(it+2)
-  // and V(it+1) into the slots freed by tiles it-1 and it-2.  S = Q.K^T(it) on the matrix cores;
+  // and V(it+1) into the slots freed by tiles it-1 and it-2.  CUR and PREV say
+  // whether tiles it and it-1 are core tiles (fp16 operands) or raw tiles
+  // (bf16).  S = Q.K^T(it) on the matrix cores;
   // then tile it's softmax on the vector ALUs while the matrix cores run P.V
   // of tile it-1.  Chunk cc of pr is consumed by that P.V just before tile
   // it's chunk cc overwrites it.  The rescale a new max demands (alpha) is
@@ -325,7 +339,8 @@ void prefill_mfma_kernel(PrefillParams P) {
   bool grow_pending = false;
   float alpha_pending = 1.0f;
   int kslot = 0;  // it % 3
-  auto iteration = [&](int it) {
+  auto iteration = [&](int it, auto cur_tag, auto prev_tag) {
+    constexpr bool CUR = decltype(cur_tag)::value, PREV = decltype(prev_tag)::value;
     const int prev = kslot == 0 ? 2 : kslot - 1, next = kslot == 2 ? 0 : kslot + 1;
     load_k(prev, it + 2);  // empty (zeros) past the last tile
     load_v(next, it + 1);
@@ -349,16 +364,15 @@ void prefill_mfma_kernel(PrefillParams P) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + (32 * kb + j) * KRow + (16 * ks + 8 * hh) * 2);
-        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb, sx[kb], 0, 0, 0);
+        sx[kb] = mfma32<CUR>(a, qb, sx[kb]);
       }
     }
-    if (!tile_full(it)) {
+    if (!tile_full(it, CUR)) {
       // key kk of the tile is visible to this lane's row iff lo_rel <= kk <= hi_rel
       asm volatile("" ::: "memory");  // keeps this a real (scalar) branch
       const int base = tile_base(it);
-      const bool core = tile_core(it);
-      const int lo_rel = core ? 0 : my_lo - base;
-      const int hi_rel = core ? my_nc - 1 - base : t - base;
+      const int lo_rel = CUR ? 0 : my_lo - base;
+      const int hi_rel = CUR ? my_nc - 1 - base : t - base;
       const unsigned span = (unsigned)(hi_rel - lo_rel);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -389,6 +403,8 @@ void prefill_mfma_kernel(PrefillParams P) {
     // each MFMA (32 cycles on the matrix core) come the probabilities it can
     // hide (2 fma, 2 exp, 1 convert per pair).  sched_barrier freezes
     // that order; V^T fragments are read two MFMAs ahead through a ring of 3.
+    // The P.V and row-sum MFMAs take tile it-1's operand type, the new
+    // probabilities tile it's.
     static_assert(DB == 2 || DB == 4, "head dim 64 or 128");
     constexpr int PPM = 8 / DB;  // probabilities per MFMA slot
     constexpr int NPV = 4 * DB;  // P.V MFMAs per tile
@@ -398,34 +414,41 @@ void prefill_mfma_kernel(PrefillParams P) {
     ring[1] = vfrag(1);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      bf16x8 pnew;
+      u32x4 pnew;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int n = cc * DB + db;
         if (n + 2 < NPV) ring[(n + 2) % 3] = vfrag(n + 2);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % 3], pr[cc], o[db], 0, 0, 0);
+        o[db] = mfma32<PREV>(ring[n % 3], pr[cc], o[db]);
 #pragma unroll
         for (int e = db * PPM; e < db * PPM + PPM; e += 2) {
           const int r = (cc & 1) * 8 + e;
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r], c, -mc));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r + 1], c, -mc));
-          bf16x2 pk;
-          pk[0] = static_cast<__bf16>(p0);
-          pk[1] = static_cast<__bf16>(p1);
-          pnew[e] = pk[0];
-          pnew[e + 1] = pk[1];
+          pnew[e >> 1] = pack_op<CUR>(p0, p1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      row_sum_mfma(pr[cc]);  // tile it-1's chunk cc, then replaced by tile it's
-      pr[cc] = pnew;
+      lsum = mfma16<PREV>(PREV ? sel_h : sel_bf, pr[cc], lsum);  // tile it-1's chunk cc, then replaced by tile it's
+      pr[cc] = __builtin_bit_cast(bf16x8, pnew);
     }
     grow_pending = __builtin_amdgcn_ballot_w64(grow) != 0;
     alpha_pending = alpha;
     kslot = next;
     sync_stage();
   };
-  for (int it = 0; it < n_tiles; ++it) iteration(it);
+  // core tiles on fp16 Q fragments, then the raw tiles on bf16 ones ("tile
+  // -1" holds zero probabilities, which read the same in either type)
+  int it = 0;
+  if (n_ct > 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16_frag_to_f16(qf[ks]);
+    for (; it < n_ct; ++it) iteration(it, CoreTile{}, CoreTile{});
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = f16_frag_to_bf16(qf[ks]);
+    iteration(it++, RawTile{}, CoreTile{});
+  }
+  for (; it < n_tiles; ++it) iteration(it, RawTile{}, RawTile{});
   // the loads issued for tiles past the end must land before the workgroup's
   // LDS can be handed to another
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -436,16 +459,17 @@ void prefill_mfma_kernel(PrefillParams P) {
       for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
     rescale_sums(alpha_pending);
   }
-  {
+  auto last_tile = [&](auto core_tag) {
+    constexpr bool LAST = decltype(core_tag)::value;
     const char* vt = vbuf(kslot == 0 ? 2 : kslot - 1);  // V(n_tiles - 1)
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag_at(vt, cc, db), pr[cc], o[db], 0, 0, 0);
+      for (int db = 0; db < DB; ++db) o[db] = mfma32<LAST>(vfrag_at(vt, cc, db), pr[cc], o[db]);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) row_sum_mfma(pr[cc]);
-  }
+    for (int cc = 0; cc < 4; ++cc) lsum = mfma16<LAST>(LAST ? sel_h : sel_bf, pr[cc], lsum);
+  };
+  last_tile(RawTile{});  // the walk always ends on a raw tile (every row sees itself)
 
   // ---- normalise and store: lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
   // row j's sum: lane j%16 holds it, in lsum[0] for j < 16 and lsum[1] above

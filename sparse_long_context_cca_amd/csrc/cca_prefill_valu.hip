@@ -60,8 +60,10 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
   const T* q = static_cast<const T*>(q_);
   const T* kk = static_cast<const T*>(k_);
   const T* vv = static_cast<const T*>(v_);
-  const T* ck = static_cast<const T*>(ck_);
-  const T* cv = static_cast<const T*>(cv_);
+  // the core cache: fp32 for fp32 inputs, fp16 for bf16 inputs
+  typedef Elem<core_dt(DT)> EC;
+  const typename EC::T* ck = static_cast<const typename EC::T*>(ck_);
+  const typename EC::T* cv = static_cast<const typename EC::T*>(cv_);
 
   float qr[DH], acc[DH];
   const long qrow = ((long)(b * Hq + h) * Lq + (t - qs)) * D + half * DH;
@@ -90,8 +92,8 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(
       float kx = 0.f, vx = 0.f;
       if (f < nc_hi) {
         const long off = (kv_base * m_cap + f) * D + e;
-        kx = E::load(ck, off);
-        vx = E::load(cv, off);
+        kx = EC::load(ck, off);
+        vx = EC::load(cv, off);
       } else if (f < total) {
         const long off = (kv_base * Lk + raw_lo + (f - nc_hi)) * D + e;
         kx = E::load(kk, off);

@@ -202,3 +202,21 @@ def test_decode_workspace_size(cca_lib):
 def test_visibility_validation(cca_lib, args, code):
     assert cca_lib.cca_visibility_table(*args, P(FAKE), P(FAKE), P(FAKE), None) == code
     assert cca_lib.cca_visibility_table(10, 4, 4, P(None), P(FAKE), P(FAKE), None) == INV
+
+
+def test_core_dtype_export(cca_lib):
+    """fp32 inputs keep fp32 cores; bf16 inputs get fp16 cores; anything else is -1."""
+    assert cca_lib.cca_core_dtype(0) == 0
+    assert cca_lib.cca_core_dtype(1) == 2
+    assert cca_lib.cca_core_dtype(2) == -1 and cca_lib.cca_core_dtype(-1) == -1
+
+
+def test_backward_workspace_size(cca_lib):
+    """fp32: row statistics + fp32 core gradients; bf16 adds fp16 copies of q and
+    dout from a 256-byte boundary."""
+    f = cca_lib.cca_attn_backward_workspace_bytes
+    B, Hq, Hkv, L, d, g = 1, 32, 8, 1001, 128, 16
+    f32_part = (2 * B * Hq * L + 2 * B * Hkv * (L // g) * d) * 4
+    assert f(B, Hq, Hkv, L, d, g, 0) == f32_part
+    assert f(B, Hq, Hkv, L, d, g, 1) == (f32_part + 255) // 256 * 256 + 2 * B * Hq * L * d * 2
+    assert f(B, Hq, Hkv, L, d, g, 2) == 0 and f(0, Hq, Hkv, L, d, g, 1) == 0

@@ -40,7 +40,7 @@ def run(dt, B, Hq, Hkv, L, d, g, w, mode, seed):
     dO = torch.from_numpy(cca_inputs.normal_f32(seed + 77, (B, Hq, L, d), 1.0)).to(q.dtype)
     qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), dO.to(DEV)
     m_cap = max(L // g, 1)
-    ck = torch.zeros((B, Hkv, m_cap, d), dtype=q.dtype, device=DEV)
+    ck = torch.zeros((B, Hkv, m_cap, d), dtype=cca.core_dtype(q.dtype), device=DEV)
     cv = torch.zeros_like(ck)
     out = torch.empty_like(qd)
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=DEV)
@@ -49,7 +49,7 @@ def run(dt, B, Hq, Hkv, L, d, g, w, mode, seed):
     dq = torch.full((B, Hq, L, d), float("nan"), device=DEV)
     dk = torch.full((B, Hkv, L, d), float("nan"), device=DEV)
     dv = torch.full_like(dk, float("nan"))
-    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g, q.dtype), dtype=torch.uint8, device=DEV)
     cca.cca_attn_backward(qd, kd, vd, ck, cv, out, lse, gd, dq, dk, dv, ws, g, w, pool_mode=mode)
     torch.cuda.synchronize()
     Q, K, V, G = f32np(q), f32np(k), f32np(v), f32np(dO)
@@ -132,7 +132,7 @@ def test_backward_full_size():
     qd, kd, vd, gd = q.to(DEV), k.to(DEV), v.to(DEV), dO.to(DEV)
     say("  pool, forward with statistics, backward on GPU")
     m = L // g
-    ck = torch.empty((B, Hkv, m, d), dtype=q.dtype, device=DEV)
+    ck = torch.empty((B, Hkv, m, d), dtype=cca.core_dtype(q.dtype), device=DEV)
     cv = torch.empty_like(ck)
     out = torch.empty_like(qd)
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=DEV)
@@ -141,7 +141,7 @@ def test_backward_full_size():
     dq = torch.empty((B, Hq, L, d), dtype=torch.float32, device=DEV)
     dk = torch.empty((B, Hkv, L, d), dtype=torch.float32, device=DEV)
     dv = torch.empty_like(dk)
-    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g, q.dtype), dtype=torch.uint8, device=DEV)
     cca.cca_attn_backward(qd, kd, vd, ck, cv, out, lse, gd, dq, dk, dv, ws, g, w)
     torch.cuda.synchronize()
     hk = 0

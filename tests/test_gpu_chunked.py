@@ -46,12 +46,15 @@ def i32(x):
 
 
 def check_cores(dt, got, ref, mode):
+    """Cores in the core dtype (fp16 for bf16 inputs): max pooling equals the
+    oracle's maximum rounded to it, the other rules lie within half an ulp."""
     if mode == cca.CCA_POOL_MAX:
-        assert np.array_equal(host(got), ref)
+        cdt = torch.float32 if dt == "f32" else torch.float16
+        assert np.array_equal(host(got), torch.from_numpy(ref).to(cdt).to(torch.float64).numpy())
     elif dt == "f32":
         assert float(np.abs(host(got) - ref).max()) <= 1e-5
     else:
-        assert np.all(np.abs(host(got) - ref) <= np.abs(ref) * 2.0 ** -8 * 1.01 + 1e-6)
+        assert np.all(np.abs(host(got) - ref) <= np.abs(ref) * 2.0 ** -11 * 1.01 + 1e-6)
 
 
 CHUNK_CASES = [
@@ -73,7 +76,7 @@ def test_chunked_prefill_equals_full_prefill(case):
     q, k, v = inputs(dt, B, Hq, Hkv, L, d, g, w, seed=700 + L)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     m_cap = L // g + 2
-    ck = torch.full((B, Hkv, m_cap, d), float("nan"), dtype=q.dtype, device=DEV)
+    ck = torch.full((B, Hkv, m_cap, d), float("nan"), dtype=cca.core_dtype(q.dtype), device=DEV)
     cv = torch.full_like(ck, float("nan"))
     out = torch.full((B, Hq, L, d), float("nan"), dtype=q.dtype, device=DEV)
     start = 0
@@ -109,7 +112,7 @@ def test_variable_length_batch():
     q, k, v = inputs(dt, B, Hq, Hkv, L, d, g, w, seed=811)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     m_cap = L // g
-    ck = torch.full((B, Hkv, m_cap, d), float("nan"), dtype=q.dtype, device=DEV)
+    ck = torch.full((B, Hkv, m_cap, d), float("nan"), dtype=cca.core_dtype(q.dtype), device=DEV)
     cv = torch.full_like(ck, float("nan"))
     steps = [([0, 0, 0], [100, 250, 0]), ([100, 250, 0], [200, 50, 300]), ([300, 300, 300], [0, 277, 3])]
     got = {b: [] for b in range(B)}
@@ -143,7 +146,7 @@ def test_ranges_that_do_not_fit_give_nan_and_no_writes():
     say("chunk ranges that do not fit")
     mk = lambda *s: torch.ones(s, dtype=torch.bfloat16, device=DEV)
     q, k, v = mk(B, Hq, Lq, d), mk(B, Hkv, Lk, d), mk(B, Hkv, Lk, d)
-    ck, cv = torch.zeros((B, Hkv, m_cap, d), dtype=torch.bfloat16, device=DEV), torch.zeros((B, Hkv, m_cap, d), dtype=torch.bfloat16, device=DEV)
+    ck, cv = torch.zeros((B, Hkv, m_cap, d), dtype=torch.float16, device=DEV), torch.zeros((B, Hkv, m_cap, d), dtype=torch.float16, device=DEV)
     out = torch.zeros((B, Hq, Lq, d), dtype=torch.bfloat16, device=DEV)
     # b0 fits; b1 q_len > Lq; b2 q_start + q_len > Lk; b3 sees a core beyond m_cap
     qs, ql = i32([0, 0, 250, 192]), i32([64, 65, 10, 64])
@@ -169,7 +172,7 @@ def test_prefill_decode_handoff(dt):
     q, k, v = inputs(dt, B, Hq, Hkv, T, d, g, w, seed=919)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     m_cap = T // g + 1
-    ck = torch.zeros((B, Hkv, m_cap, d), dtype=q.dtype, device=DEV)
+    ck = torch.zeros((B, Hkv, m_cap, d), dtype=cca.core_dtype(q.dtype), device=DEV)
     cv = torch.zeros_like(ck)
     # prefill in two chunks per sequence: 128 rows, then the rest
     for starts, ln in (([0, 0], [128, 128]), ([128, 128], [lens[0] - 128, lens[1] - 128])):
@@ -221,7 +224,7 @@ def test_chunked_full_size_is_bit_identical_to_full_prefill():
     del q, k, v
     B, Hkv, d, g, w = cfg.B, cfg.Hkv, cfg.d, cfg.g, cfg.w
     m = cfg.L // g
-    ck_full = torch.empty((B, Hkv, m, d), dtype=qd.dtype, device=DEV)
+    ck_full = torch.empty((B, Hkv, m, d), dtype=cca.core_dtype(qd.dtype), device=DEV)
     cv_full = torch.empty_like(ck_full)
     out_full = torch.empty_like(qd)
     cca.cca_pool_core(qd, kd, vd, ck_full, cv_full, g)

@@ -55,7 +55,7 @@ def test_offsets_beyond_2_31_elements():
         dO[b : b + 1].copy_(gs.to(DEV))
         host[b] = (f32np(qs), f32np(ks), f32np(vs), f32np(gs))
     m = L // g
-    ck = torch.empty((B, Hkv, m, d), dtype=bf, device=DEV)
+    ck = torch.empty((B, Hkv, m, d), dtype=cca.core_dtype(bf), device=DEV)
     cv = torch.empty_like(ck)
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=DEV)
@@ -65,7 +65,7 @@ def test_offsets_beyond_2_31_elements():
     dq = torch.empty((B, Hq, L, d), dtype=torch.float32, device=DEV)
     dk = torch.empty((B, Hkv, L, d), dtype=torch.float32, device=DEV)
     dv = torch.empty_like(dk)
-    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g, bf), dtype=torch.uint8, device=DEV)
     cca.cca_attn_backward(q, k, v, ck, cv, out, lse, dO, dq, dk, dv, ws, g, w)
     torch.cuda.synchronize()
 
