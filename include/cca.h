@@ -331,6 +331,32 @@ cca_status cca_attn_decode_ex(const void* q_t, const void* k_t, const void* v_t,
                               void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                               int d, int g, int w, cca_dtype dt, int pool_mode, void* stream);
 
+/*
+ * cca_attn_decode_scratch - cca_attn_decode_ex for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid it): the same step, with the
+ * split-K states in a fixed device array of the library (cca_decode_scratch_bytes()
+ * bytes, 16 MiB) instead of a caller workspace.  Nothing is allocated or freed
+ * by this call or by the library.  Each GPU holds its own copy of the array
+ * from its first use until the process ends; its address is looked up once
+ * per device (the calling thread's current device).  Every call on one GPU
+ * shares that array, so calls that overlap on one GPU (other streams, other
+ * threads) race: the caller orders them.  The states need no clearing (every
+ * call writes all it reads).  q_t .. out, the sizes, dt and pool_mode as
+ * cca_attn_decode_ex.
+ * Errors: as cca_attn_decode_ex; CAPACITY when the split states of these
+ *   shapes (cca_decode_workspace_bytes) exceed the array; HIP when the array's
+ *   address cannot be found on the current device.
+ */
+cca_status cca_attn_decode_scratch(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                                   void* ring_v, int R, void* core_k, void* core_v, int m_cap,
+                                   int32_t* pos, int advance_pos, void* out, cca_dtype out_dt, int B,
+                                   int Hq, int Hkv, int d, int g, int w, cca_dtype dt, int pool_mode,
+                                   void* stream);
+
+/* Size in bytes of the fixed device array cca_attn_decode_scratch uses. */
+size_t cca_decode_scratch_bytes(void);
+
 #ifdef __cplusplus
 }
 #endif

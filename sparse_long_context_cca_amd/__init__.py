@@ -9,5 +9,6 @@ from ._lib import (  # noqa: F401
     EXPORTS, LIB_PATH, cca_attn_backward, cca_attn_backward_workspace_bytes, cca_attn_decode,
     cca_attn_prefill, cca_attn_prefill_chunk, cca_attn_prefill_train,
     cca_cache_fill_ring, cca_pool_core_chunk,
-    cca_decode_workspace_bytes, cca_pool_core, cca_version, cca_visibility_table, core_dtype, load,
+    cca_attn_decode_scratch, cca_decode_scratch_bytes, cca_decode_workspace_bytes, cca_pool_core,
+    cca_version, cca_visibility_table, core_dtype, load,
 )

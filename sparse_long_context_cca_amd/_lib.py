@@ -28,7 +28,8 @@ EXPORTS = ["cca_version", "cca_status_string", "cca_last_error", "cca_core_dtype
            "cca_pool_core", "cca_pool_core_ex", "cca_attn_prefill", "cca_attn_prefill_ex",
            "cca_decode_workspace_bytes", "cca_attn_decode", "cca_attn_decode_ex",
            "cca_pool_core_chunk", "cca_attn_prefill_chunk", "cca_cache_fill_ring",
-           "cca_attn_prefill_train", "cca_attn_backward_workspace_bytes", "cca_attn_backward"]
+           "cca_attn_prefill_train", "cca_attn_backward_workspace_bytes", "cca_attn_backward",
+           "cca_attn_decode_scratch", "cca_decode_scratch_bytes"]
 
 
 class CCAError(RuntimeError):
@@ -69,6 +70,8 @@ def load() -> ctypes.CDLL:
         "cca_attn_prefill_train": ([P, P, P, P, P, I, P, I, P, I, I, I, I, I, I, I, I, P], I),
         "cca_attn_backward_workspace_bytes": ([I, I, I, I, I, I, I], S),
         "cca_attn_backward": ([P, P, P, P, P, I, P, P, P, P, P, P, P, S, I, I, I, I, I, I, I, I, I, P], I),
+        "cca_attn_decode_scratch": ([P, P, P, P, P, I, P, P, I, P, I, P, I, I, I, I, I, I, I, I, I, P], I),
+        "cca_decode_scratch_bytes": ([], S),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -242,6 +245,33 @@ def cca_attn_decode(q_t, k_t, v_t, ring_k, ring_v, core_k, core_v, pos, out, wor
                                      _ptr(out), _dt(out), _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), B, Hq, Hkv, d, g,
                                      w, _dt(q_t), pool_mode, _stream(stream)))
+
+
+def cca_decode_scratch_bytes() -> int:
+    return int(load().cca_decode_scratch_bytes())
+
+
+def cca_attn_decode_scratch(q_t, k_t, v_t, ring_k, ring_v, core_k, core_v, pos, out, g: int, w: int,
+                            advance_pos: bool = False, pool_mode: int = CCA_POOL_SOFTMAX,
+                            stream=None) -> None:
+    """cca_attn_decode without a workspace: the split states live in the library's fixed device
+    array (for callers that cannot allocate; calls that overlap on one GPU race)."""
+    B, Hq, d = _dims(q_t, 3, "q_t")
+    Hkv = _dims(k_t, 3, "k_t")[1]
+    R = _dims(ring_k, 4, "ring_k")[2]
+    m_cap = core_k.shape[2] if core_k is not None else 0
+    dt = (q_t.dtype,)
+    spec = [("q_t", q_t, (B, Hq, d), _FLOAT), ("k_t", k_t, (B, Hkv, d), dt), ("v_t", v_t, (B, Hkv, d), dt),
+            ("ring_k", ring_k, (B, Hkv, R, d), dt), ("ring_v", ring_v, (B, Hkv, R, d), dt),
+            ("pos", pos, (B,), (torch.int32,)), ("out", out, (B, Hq, d), (q_t.dtype, torch.float32))]
+    if core_k is not None or core_v is not None:
+        ct = (core_dtype(q_t.dtype),)
+        spec += [("core_k", core_k, (B, Hkv, m_cap, d), ct), ("core_v", core_v, (B, Hkv, m_cap, d), ct)]
+    _expect(spec)
+    _check(load().cca_attn_decode_scratch(_ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(ring_k), _ptr(ring_v), R,
+                                          _ptr(core_k), _ptr(core_v), m_cap, _ptr(pos), int(advance_pos),
+                                          _ptr(out), _dt(out), B, Hq, Hkv, d, g, w, _dt(q_t), pool_mode,
+                                          _stream(stream)))
 
 
 def _rows(t):

@@ -444,7 +444,7 @@ cca_status attn_decode(const char* fn, const void* q_t, const void* k_t, const v
                        void* ring_k, void* ring_v, int R, void* core_k, void* core_v, int m_cap,
                        int32_t* pos, int advance_pos, void* out, cca_dtype out_dt, void* workspace,
                        size_t workspace_bytes, int B, int Hq, int Hkv, int d, int g, int w,
-                       cca_dtype dt, int pool_mode, void* stream) {
+                       cca_dtype dt, int pool_mode, void* stream, bool use_scratch = false) {
   if (g < 1 || w < 1) return fail(CCA_ERR_INVALID_ARG, "%s: g=%d w=%d must be >= 1", fn, g, w);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
   if (st != CCA_OK) return st;
@@ -474,10 +474,19 @@ cca_status attn_decode(const char* fn, const void* q_t, const void* k_t, const v
                    (long long)B * Hq * d);
   if (st != CCA_OK) return st;
   cca::DecodePlan plan = cca::decode_plan(B, Hq, Hkv, d, m_cap, g, w);
-  if (workspace_bytes < plan.ws_bytes)
-    return fail(CCA_ERR_CAPACITY, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes,
-                plan.ws_bytes);
-  if (plan.ws_bytes > 0) REQUIRE_PTR(workspace);
+  if (use_scratch) {
+    // the split states go to the library's fixed device scratch
+    if (plan.ws_bytes > cca::kDecodeScratchBytes)
+      return fail(CCA_ERR_CAPACITY, "%s: the split states need %zu bytes, beyond the %zu-byte scratch", fn,
+                  plan.ws_bytes, cca::kDecodeScratchBytes);
+    const hipError_t e = cca::decode_scratch(&workspace);
+    if (e != hipSuccess) return from_hip(e, fn);
+  } else {
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(CCA_ERR_CAPACITY, "%s: workspace %zu bytes < %zu needed", fn, workspace_bytes,
+                  plan.ws_bytes);
+    if (plan.ws_bytes > 0) REQUIRE_PTR(workspace);
+  }
   cca::Shape sh{B, Hq, Hkv, 0, d, g, w};
   return from_hip(cca::launch_decode(q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v, m_cap, pos,
                                      advance_pos, out, out_dt, workspace, plan, sh, dt, pool_mode,
@@ -506,5 +515,17 @@ cca_status cca_attn_decode_ex(const void* q_t, const void* k_t, const void* v_t,
                      pos, advance_pos, out, out_dt, workspace, workspace_bytes, B, Hq, Hkv, d, g, w,
                      dt, pool_mode, stream);
 }
+
+cca_status cca_attn_decode_scratch(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
+                                   void* ring_v, int R, void* core_k, void* core_v, int m_cap,
+                                   int32_t* pos, int advance_pos, void* out, cca_dtype out_dt, int B,
+                                   int Hq, int Hkv, int d, int g, int w, cca_dtype dt, int pool_mode,
+                                   void* stream) {
+  return attn_decode("cca_attn_decode_scratch", q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v,
+                     m_cap, pos, advance_pos, out, out_dt, nullptr, 0, B, Hq, Hkv, d, g, w, dt,
+                     pool_mode, stream, true);
+}
+
+size_t cca_decode_scratch_bytes(void) { return cca::kDecodeScratchBytes; }
 
 }  // extern "C"

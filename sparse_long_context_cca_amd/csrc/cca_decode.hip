@@ -18,6 +18,7 @@
 //   optionally advances pos[b].
 // HBM-bound: every visible K/V byte is read once per step.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "cca_device.hpp"
@@ -682,6 +683,33 @@ hipError_t launch_fill_ring(const void* k, const void* v, void* ring_k, void* ri
                      static_cast<char*>(ring_k), static_cast<char*>(ring_v), R, seq_len, Hkv, Lk,
                      row_bytes);
   return hipGetLastError();
+}
+
+// ---- fixed device scratch for callers that cannot allocate
+// The split states of cca_attn_decode_scratch live in this array: one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is a stand-in, not a device address): the
+// device address is looked up once per device with hipGetSymbolAddress, with
+// that device current, and kept.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int m_cap, int g, int w) {

@@ -55,6 +55,12 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int B, int Hq, int Hkv, int d, int m_cap, int g, int w);
 
+// Device scratch of cca_attn_decode_scratch (a fixed array in cca_decode.hip,
+// one per GPU): its device address on the current device, looked up once per
+// device.  Calls that overlap on one GPU share it and race.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
+
 hipError_t launch_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                          void* ring_v, int R, void* ck, void* cv, int m_cap, int32_t* pos,
                          int advance_pos, void* out, int out_dt, void* ws, const DecodePlan& plan,

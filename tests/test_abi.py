@@ -220,3 +220,17 @@ def test_backward_workspace_size(cca_lib):
     assert f(B, Hq, Hkv, L, d, g, 0) == f32_part
     assert f(B, Hq, Hkv, L, d, g, 1) == (f32_part + 255) // 256 * 256 + 2 * B * Hq * L * d * 2
     assert f(B, Hq, Hkv, L, d, g, 2) == 0 and f(0, Hq, Hkv, L, d, g, 1) == 0
+
+
+def test_decode_scratch_rejects_states_beyond_its_array(cca_lib):
+    """The allocation-free decode refuses shapes whose split states exceed its
+    fixed array, before anything touches the GPU."""
+    cap = cca_lib.cca_decode_scratch_bytes()
+    assert cap == 16 << 20
+    f = cca_lib.cca_decode_workspace_bytes
+    B, Hq, Hkv, d, m_cap, g, w = 512, 64, 8, 128, 64, 16, 64
+    assert f(B, Hq, Hkv, d, m_cap, g, w) > cap
+    st = cca_lib.cca_attn_decode_scratch(P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 64, P(FAKE), P(FAKE), m_cap,
+                                         P(FAKE), 1, P(FAKE), 1, B, Hq, Hkv, d, g, w, 1, 0, None)
+    assert st == CAP
+    assert b"scratch" in cca_lib.cca_last_error()
