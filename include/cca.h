@@ -73,7 +73,8 @@ typedef enum cca_status {
 } cca_status;
 
 /* Element types.  CCA_F16 names the core cache of bf16 inputs only; it is not
- * accepted as an input or output dtype. */
+ * accepted as an input or output dtype.  Entry points take dtypes as int, so
+ * that any value a caller passes is checked rather than undefined. */
 typedef enum cca_dtype { CCA_F32 = 0, CCA_BF16 = 1, CCA_F16 = 2 } cca_dtype;
 
 /*
@@ -134,7 +135,7 @@ cca_status cca_visibility_table(int L, int g, int w, int32_t* n_core, int32_t* w
  */
 cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core_k, void* core_v,
                          int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d, int g,
-                         cca_dtype dt, void* stream);
+                         int dt, void* stream);
 
 /*
  * cca_pool_core_ex - cca_pool_core with a pooling rule (cca_pool_mode above).
@@ -145,7 +146,7 @@ cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core
  */
 cca_status cca_pool_core_ex(const void* q, const void* k, const void* v, void* core_k,
                             void* core_v, int m_cap, float* weights, int B, int Hq, int Hkv, int L,
-                            int d, int g, cca_dtype dt, int mode, void* stream);
+                            int d, int g, int dt, int mode, void* stream);
 
 /*
  * cca_attn_prefill - causal prefill of the fused CCA attention (digest,
@@ -157,8 +158,8 @@ cca_status cca_pool_core_ex(const void* q, const void* k, const void* v, void* c
  * Errors: as cca_pool_core, plus INVALID_ARG for w < 1 or a bad out_dt.
  */
 cca_status cca_attn_prefill(const void* q, const void* k, const void* v, const void* core_k,
-                            const void* core_v, int m_cap, void* out, cca_dtype out_dt, int B,
-                            int Hq, int Hkv, int L, int d, int g, int w, cca_dtype dt,
+                            const void* core_v, int m_cap, void* out, int out_dt, int B,
+                            int Hq, int Hkv, int L, int d, int g, int w, int dt,
                             void* stream);
 
 /*
@@ -168,8 +169,8 @@ cca_status cca_attn_prefill(const void* q, const void* k, const void* v, const v
  * UNSUPPORTED if the choice does not fit dt.
  */
 cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, const void* core_k,
-                               const void* core_v, int m_cap, void* out, cca_dtype out_dt, int B,
-                               int Hq, int Hkv, int L, int d, int g, int w, cca_dtype dt,
+                               const void* core_v, int m_cap, void* out, int out_dt, int B,
+                               int Hq, int Hkv, int L, int d, int g, int w, int dt,
                                int kernel, void* stream);
 
 /*
@@ -184,9 +185,9 @@ cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, cons
  *   scores q_t . key / sqrt(d) over its visible keys.
  */
 cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, const void* core_k,
-                                  const void* core_v, int m_cap, void* out, cca_dtype out_dt,
+                                  const void* core_v, int m_cap, void* out, int out_dt,
                                   float* lse, int B, int Hq, int Hkv, int L, int d, int g, int w,
-                                  cca_dtype dt, void* stream);
+                                  int dt, void* stream);
 
 /*
  * cca_attn_backward_workspace_bytes - device workspace cca_attn_backward needs
@@ -196,7 +197,7 @@ cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, c
  *   the fp16 cores read; 0 for sizes below 1 or an unknown dt.
  */
 size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g,
-                                         cca_dtype dt);
+                                         int dt);
 
 /*
  * cca_attn_backward - gradients of the whole forward (pooling with rule
@@ -219,7 +220,7 @@ cca_status cca_attn_backward(const void* q, const void* k, const void* v, const 
                              const void* core_v, int m_cap, const void* out, const float* lse,
                              const void* dout, float* dq, float* dk, float* dv, void* workspace,
                              size_t workspace_bytes, int B, int Hq, int Hkv, int L, int d, int g,
-                             int w, cca_dtype dt, int pool_mode, void* stream);
+                             int w, int dt, int pool_mode, void* stream);
 
 /*
  * Chunked and variable-length prefill.  The article notes that CCA generates
@@ -246,7 +247,7 @@ cca_status cca_attn_backward(const void* q, const void* k, const void* v, const 
 cca_status cca_pool_core_chunk(const void* q, const void* k, const void* v, void* core_k,
                                void* core_v, int m_cap, const int32_t* q_start,
                                const int32_t* q_len, int B, int Hq, int Hkv, int Lq, int Lk, int d,
-                               int g, cca_dtype dt, int mode, void* stream);
+                               int g, int dt, int mode, void* stream);
 
 /*
  * cca_attn_prefill_chunk - the fused attention rows of the covered positions
@@ -258,9 +259,9 @@ cca_status cca_pool_core_chunk(const void* q, const void* k, const void* v, void
  *   m_cap < 0), UNSUPPORTED as cca_attn_prefill.
  */
 cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, const void* core_k,
-                                  const void* core_v, int m_cap, void* out, cca_dtype out_dt,
+                                  const void* core_v, int m_cap, void* out, int out_dt,
                                   const int32_t* q_start, const int32_t* q_len, int B, int Hq,
-                                  int Hkv, int Lq, int Lk, int d, int g, int w, cca_dtype dt,
+                                  int Hkv, int Lq, int Lk, int d, int g, int w, int dt,
                                   void* stream);
 
 /*
@@ -273,7 +274,7 @@ cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, c
  *   (d, dt, B*Hkv > 65535).
  */
 cca_status cca_cache_fill_ring(const void* k, const void* v, void* ring_k, void* ring_v, int R,
-                               const int32_t* seq_len, int B, int Hkv, int Lk, int d, cca_dtype dt,
+                               const int32_t* seq_len, int B, int Hkv, int Lk, int d, int dt,
                                void* stream);
 
 /*
@@ -314,9 +315,9 @@ size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int 
  */
 cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                            void* ring_v, int R, void* core_k, void* core_v, int m_cap,
-                           int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                           int32_t* pos, int advance_pos, void* out, int out_dt,
                            void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
-                           int g, int w, cca_dtype dt, void* stream);
+                           int g, int w, int dt, void* stream);
 
 /*
  * cca_attn_decode_ex - cca_attn_decode whose on-completion pooling (step 2)
@@ -327,9 +328,9 @@ cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, vo
  */
 cca_status cca_attn_decode_ex(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                               void* ring_v, int R, void* core_k, void* core_v, int m_cap,
-                              int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                              int32_t* pos, int advance_pos, void* out, int out_dt,
                               void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                              int d, int g, int w, cca_dtype dt, int pool_mode, void* stream);
+                              int d, int g, int w, int dt, int pool_mode, void* stream);
 
 /*
  * cca_attn_decode_scratch - cca_attn_decode_ex for callers that cannot
@@ -350,8 +351,8 @@ cca_status cca_attn_decode_ex(const void* q_t, const void* k_t, const void* v_t,
  */
 cca_status cca_attn_decode_scratch(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                                    void* ring_v, int R, void* core_k, void* core_v, int m_cap,
-                                   int32_t* pos, int advance_pos, void* out, cca_dtype out_dt, int B,
-                                   int Hq, int Hkv, int d, int g, int w, cca_dtype dt, int pool_mode,
+                                   int32_t* pos, int advance_pos, void* out, int out_dt, int B,
+                                   int Hq, int Hkv, int d, int g, int w, int dt, int pool_mode,
                                    void* stream);
 
 /* Size in bytes of the fixed device array cca_attn_decode_scratch uses. */

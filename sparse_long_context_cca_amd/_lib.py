@@ -18,7 +18,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcca.so")
+# CCA_LIB_PATH selects another build of the same library (the CPU tests point
+# it at the host-sanitized build); there is no fallback either way.
+LIB_PATH = os.environ.get("CCA_LIB_PATH") or os.path.join(_PKG, "libcca.so")
 
 CCA_OK, CCA_ERR_INVALID_ARG, CCA_ERR_UNSUPPORTED, CCA_ERR_CAPACITY, CCA_ERR_HIP = range(5)
 CCA_F32, CCA_BF16, CCA_F16 = 0, 1, 2

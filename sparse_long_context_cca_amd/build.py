@@ -43,8 +43,50 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Host-side checking build: the argument validation of the C ABI (cca_api.hip)
+# compiled with AddressSanitizer and UndefinedBehaviorSanitizer on its host
+# code only (each -fsanitize follows -Xarch_host; device code is built as
+# usual) and linked with the regular kernel objects into a separate library.
+# The CPU tests load it with the sanitizer runtime preloaded.
+SAN_LIB = os.path.join(OBJ, "libcca_asan.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_RUNTIME = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+
+
+def sanitizer_runtime() -> str:
+    """Path of clang's shared ASan runtime (to preload into an uninstrumented Python)."""
+    for root, _, files in os.walk(SAN_RUNTIME):
+        if "libclang_rt.asan-x86_64.so" in files:
+            return os.path.join(root, "libclang_rt.asan-x86_64.so")
+    raise RuntimeError(f"libclang_rt.asan-x86_64.so not found under {SAN_RUNTIME}")
+
+
+def build_sanitized(objs=None) -> str:
+    """Builds _build/libcca_asan.so: cca_api.hip with host sanitizers, the
+    other sources as in build().  Returns its path."""
+    os.makedirs(OBJ, exist_ok=True)
+    san_obj = os.path.join(OBJ, "cca_api_asan.o")
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, "cca_api.hip"), "-o", san_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized cca_api.hip:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if objs is None:
+        objs = [_compile(s) for s in SOURCES if s != "cca_api.hip"]
+    objs = [o for o in objs if not o.endswith("cca_api.o")]
+    tmp = SAN_LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-shared-libsan", *SAN_FLAGS, san_obj, *objs,
+           "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    shutil.move(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 def build(verbose: bool = True) -> str:
-    """Compiles every source for gfx950 and links libcca.so; returns its path."""
+    """Compiles every source for gfx950 and links libcca.so (and the
+    host-sanitized libcca_asan.so for the CPU tests); returns libcca.so's path."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(OBJ, exist_ok=True)
@@ -57,8 +99,9 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     shutil.move(tmp, LIB)
+    build_sanitized(objs)
     if verbose:
-        print(f"built {LIB} from {len(objs)} sources", file=sys.stderr)
+        print(f"built {LIB} from {len(objs)} sources (and {SAN_LIB})", file=sys.stderr)
     return LIB
 
 

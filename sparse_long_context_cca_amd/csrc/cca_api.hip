@@ -136,7 +136,7 @@ cca_status check_pool_mode(const char* fn, int mode, int Hq, int Hkv) {
 
 cca_status pool_core(const char* fn, const void* q, const void* k, const void* v, void* core_k,
                      void* core_v, int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d,
-                     int g, cca_dtype dt, int mode, void* stream) {
+                     int g, int dt, int mode, void* stream) {
   if (L < 1 || g < 1) return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d must be >= 1", fn, L, g);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
   if (st != CCA_OK) return st;
@@ -182,14 +182,14 @@ cca_status check_rows(const char* fn, const int32_t* q_start, const int32_t* q_l
 
 cca_status cca_pool_core(const void* q, const void* k, const void* v, void* core_k, void* core_v,
                          int m_cap, float* weights, int B, int Hq, int Hkv, int L, int d, int g,
-                         cca_dtype dt, void* stream) {
+                         int dt, void* stream) {
   return pool_core("cca_pool_core", q, k, v, core_k, core_v, m_cap, weights, B, Hq, Hkv, L, d, g,
                    dt, CCA_POOL_SOFTMAX, stream);
 }
 
 cca_status cca_pool_core_ex(const void* q, const void* k, const void* v, void* core_k,
                             void* core_v, int m_cap, float* weights, int B, int Hq, int Hkv, int L,
-                            int d, int g, cca_dtype dt, int mode, void* stream) {
+                            int d, int g, int dt, int mode, void* stream) {
   return pool_core("cca_pool_core_ex", q, k, v, core_k, core_v, m_cap, weights, B, Hq, Hkv, L, d,
                    g, dt, mode, stream);
 }
@@ -197,7 +197,7 @@ cca_status cca_pool_core_ex(const void* q, const void* k, const void* v, void* c
 cca_status cca_pool_core_chunk(const void* q, const void* k, const void* v, void* core_k,
                                void* core_v, int m_cap, const int32_t* q_start,
                                const int32_t* q_len, int B, int Hq, int Hkv, int Lq, int Lk, int d,
-                               int g, cca_dtype dt, int mode, void* stream) {
+                               int g, int dt, int mode, void* stream) {
   const char* fn = "cca_pool_core_chunk";
   if (g < 1) return fail(CCA_ERR_INVALID_ARG, "%s: g=%d must be >= 1", fn, g);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
@@ -230,8 +230,8 @@ cca_status cca_pool_core_chunk(const void* q, const void* k, const void* v, void
 }
 
 cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, const void* core_k,
-                               const void* core_v, int m_cap, void* out, cca_dtype out_dt, int B,
-                               int Hq, int Hkv, int L, int d, int g, int w, cca_dtype dt,
+                               const void* core_v, int m_cap, void* out, int out_dt, int B,
+                               int Hq, int Hkv, int L, int d, int g, int w, int dt,
                                int kernel, void* stream) {
   const char* fn = "cca_attn_prefill";
   if (L < 1 || g < 1 || w < 1)
@@ -272,9 +272,9 @@ cca_status cca_attn_prefill_ex(const void* q, const void* k, const void* v, cons
 }
 
 cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, const void* core_k,
-                                  const void* core_v, int m_cap, void* out, cca_dtype out_dt,
+                                  const void* core_v, int m_cap, void* out, int out_dt,
                                   float* lse, int B, int Hq, int Hkv, int L, int d, int g, int w,
-                                  cca_dtype dt, void* stream) {
+                                  int dt, void* stream) {
   const char* fn = "cca_attn_prefill_train";
   if (lse == nullptr || (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
     return fail(CCA_ERR_INVALID_ARG, "%s: lse is NULL or not 4-byte aligned", fn);
@@ -310,7 +310,7 @@ cca_status cca_attn_prefill_train(const void* q, const void* k, const void* v, c
       cca::launch_prefill_valu(q, k, v, core_k, core_v, m_cap, out, out_dt, sh, rr, lse, dt, s), fn);
 }
 
-size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g, cca_dtype dt) {
+size_t cca_attn_backward_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int g, int dt) {
   if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || d < 1 || g < 1) return 0;
   if (dt != CCA_F32 && dt != CCA_BF16) return 0;
   return cca::backward_workspace_bytes(B, Hq, Hkv, L, d, g, dt);
@@ -320,7 +320,7 @@ cca_status cca_attn_backward(const void* q, const void* k, const void* v, const 
                              const void* core_v, int m_cap, const void* out, const float* lse,
                              const void* dout, float* dq, float* dk, float* dv, void* workspace,
                              size_t workspace_bytes, int B, int Hq, int Hkv, int L, int d, int g,
-                             int w, cca_dtype dt, int pool_mode, void* stream) {
+                             int w, int dt, int pool_mode, void* stream) {
   const char* fn = "cca_attn_backward";
   if (L < 1 || g < 1 || w < 1)
     return fail(CCA_ERR_INVALID_ARG, "%s: L=%d g=%d w=%d must be >= 1", fn, L, g, w);
@@ -361,9 +361,9 @@ cca_status cca_attn_backward(const void* q, const void* k, const void* v, const 
 }
 
 cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, const void* core_k,
-                                  const void* core_v, int m_cap, void* out, cca_dtype out_dt,
+                                  const void* core_v, int m_cap, void* out, int out_dt,
                                   const int32_t* q_start, const int32_t* q_len, int B, int Hq,
-                                  int Hkv, int Lq, int Lk, int d, int g, int w, cca_dtype dt,
+                                  int Hkv, int Lq, int Lk, int d, int g, int w, int dt,
                                   void* stream) {
   const char* fn = "cca_attn_prefill_chunk";
   if (g < 1 || w < 1) return fail(CCA_ERR_INVALID_ARG, "%s: g=%d w=%d must be >= 1", fn, g, w);
@@ -402,7 +402,7 @@ cca_status cca_attn_prefill_chunk(const void* q, const void* k, const void* v, c
 }
 
 cca_status cca_cache_fill_ring(const void* k, const void* v, void* ring_k, void* ring_v, int R,
-                               const int32_t* seq_len, int B, int Hkv, int Lk, int d, cca_dtype dt,
+                               const int32_t* seq_len, int B, int Hkv, int Lk, int d, int dt,
                                void* stream) {
   const char* fn = "cca_cache_fill_ring";
   cca_status st = check_heads(fn, B, Hkv, Hkv, d, dt);
@@ -426,8 +426,8 @@ cca_status cca_cache_fill_ring(const void* k, const void* v, void* ring_k, void*
 }
 
 cca_status cca_attn_prefill(const void* q, const void* k, const void* v, const void* core_k,
-                            const void* core_v, int m_cap, void* out, cca_dtype out_dt, int B,
-                            int Hq, int Hkv, int L, int d, int g, int w, cca_dtype dt,
+                            const void* core_v, int m_cap, void* out, int out_dt, int B,
+                            int Hq, int Hkv, int L, int d, int g, int w, int dt,
                             void* stream) {
   return cca_attn_prefill_ex(q, k, v, core_k, core_v, m_cap, out, out_dt, B, Hq, Hkv, L, d, g, w,
                              dt, 0, stream);
@@ -442,9 +442,9 @@ namespace {
 
 cca_status attn_decode(const char* fn, const void* q_t, const void* k_t, const void* v_t,
                        void* ring_k, void* ring_v, int R, void* core_k, void* core_v, int m_cap,
-                       int32_t* pos, int advance_pos, void* out, cca_dtype out_dt, void* workspace,
+                       int32_t* pos, int advance_pos, void* out, int out_dt, void* workspace,
                        size_t workspace_bytes, int B, int Hq, int Hkv, int d, int g, int w,
-                       cca_dtype dt, int pool_mode, void* stream, bool use_scratch = false) {
+                       int dt, int pool_mode, void* stream, bool use_scratch = false) {
   if (g < 1 || w < 1) return fail(CCA_ERR_INVALID_ARG, "%s: g=%d w=%d must be >= 1", fn, g, w);
   cca_status st = check_heads(fn, B, Hq, Hkv, d, dt);
   if (st != CCA_OK) return st;
@@ -498,9 +498,9 @@ cca_status attn_decode(const char* fn, const void* q_t, const void* k_t, const v
 
 cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                            void* ring_v, int R, void* core_k, void* core_v, int m_cap,
-                           int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                           int32_t* pos, int advance_pos, void* out, int out_dt,
                            void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int d,
-                           int g, int w, cca_dtype dt, void* stream) {
+                           int g, int w, int dt, void* stream) {
   return attn_decode("cca_attn_decode", q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v, m_cap,
                      pos, advance_pos, out, out_dt, workspace, workspace_bytes, B, Hq, Hkv, d, g, w,
                      dt, CCA_POOL_SOFTMAX, stream);
@@ -508,9 +508,9 @@ cca_status cca_attn_decode(const void* q_t, const void* k_t, const void* v_t, vo
 
 cca_status cca_attn_decode_ex(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                               void* ring_v, int R, void* core_k, void* core_v, int m_cap,
-                              int32_t* pos, int advance_pos, void* out, cca_dtype out_dt,
+                              int32_t* pos, int advance_pos, void* out, int out_dt,
                               void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                              int d, int g, int w, cca_dtype dt, int pool_mode, void* stream) {
+                              int d, int g, int w, int dt, int pool_mode, void* stream) {
   return attn_decode("cca_attn_decode_ex", q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v, m_cap,
                      pos, advance_pos, out, out_dt, workspace, workspace_bytes, B, Hq, Hkv, d, g, w,
                      dt, pool_mode, stream);
@@ -518,8 +518,8 @@ cca_status cca_attn_decode_ex(const void* q_t, const void* k_t, const void* v_t,
 
 cca_status cca_attn_decode_scratch(const void* q_t, const void* k_t, const void* v_t, void* ring_k,
                                    void* ring_v, int R, void* core_k, void* core_v, int m_cap,
-                                   int32_t* pos, int advance_pos, void* out, cca_dtype out_dt, int B,
-                                   int Hq, int Hkv, int d, int g, int w, cca_dtype dt, int pool_mode,
+                                   int32_t* pos, int advance_pos, void* out, int out_dt, int B,
+                                   int Hq, int Hkv, int d, int g, int w, int dt, int pool_mode,
                                    void* stream) {
   return attn_decode("cca_attn_decode_scratch", q_t, k_t, v_t, ring_k, ring_v, R, core_k, core_v,
                      m_cap, pos, advance_pos, out, out_dt, nullptr, 0, B, Hq, Hkv, d, g, w, dt,

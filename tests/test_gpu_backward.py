@@ -4,8 +4,12 @@ through the C ABI, against the fp64 backward oracle (oracle/cca_backward.py).
 Both sides take the same seeded input bits and the same upstream gradient.
 The GPU's backward runs on the cores and the output its forward produced
 (rounded to the storage dtype), the oracle on its own exact forward, so the
-bar is relative to the gradient's scale: max |err| <= tol * max(1, max |ref|),
-tol 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (the forward's bars).
+bar is relative to the gradient's scale: max |err| <= tol * max(1, max |ref|).
+The bars sit about 1.5x above what the kernels achieve over these cases and
+the full-size one: tol 6e-3 for bf16 inputs (largest seen 4.1e-3: P and dS
+rounded to the operand type before their products, the bf16 output, the
+fp16 cores) and 2e-6 for fp32 inputs (largest seen 3.0e-7); the row
+log-sum-exp within 5e-3 (bf16; largest seen 1.8e-3) and 1e-5 (fp32; 7.5e-7).
 """
 from __future__ import annotations
 
@@ -20,7 +24,8 @@ import sparse_long_context_cca_amd as cca
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+TOL = {"f32": 2e-6, "bf16": 6e-3}
+LSE_TOL = {"f32": 1e-5, "bf16": 5e-3}
 MODES = {cca.CCA_POOL_SOFTMAX: "softmax", cca.CCA_POOL_SOFTMAX_HEADS: "softmax_heads",
          cca.CCA_POOL_MEAN: "mean", cca.CCA_POOL_MAX: "max"}
 
@@ -98,7 +103,7 @@ def test_backward_parity(case):
     got, ref, lse, lse_ref = run(dt, B, Hq, Hkv, L, d, g, w, mode, seed=40 + L + d)
     e_lse = float(np.abs(lse.double().cpu().numpy() - lse_ref).max())
     say(f"  lse max abs err {e_lse:.3e}")
-    assert e_lse <= (1e-4 if dt == "f32" else 2e-2)
+    assert e_lse <= LSE_TOL[dt]
     for name, x, y in zip(("dq", "dk", "dv"), got, ref):
         e = rel_err(x, y)
         say(f"  {name} max err / scale {e:.3e} (scale {max(1.0, float(np.abs(y).max())):.2f})")
