@@ -280,23 +280,30 @@ def bench_backward(cca, cfg, qd, kd, vd, steps=2, warmup=1):
                     "gradients fp32"}
 
 
-def reference_rates(dev="cuda:0", n=16384, copy_bytes=1 << 30, read_bytes=1 << 31, reps=10):
+def reference_rates(dev="cuda:0", n=16384, copy_bytes=1 << 30, read_rows=65536, reps=10):
     """Measured ceilings on this GPU next to the spec peaks, each timed with
     events over `reps` runs after one warm-up: a large dense bf16 GEMM through
-    torch (hipBLASLt), a device-to-device copy (read + write), and a read-only
-    stream (torch's sum over a fp32 buffer, which reads every byte once and
-    writes one value) -- the ceiling for kernels that only read, like decode."""
+    torch (hipBLASLt), a device-to-device copy (read + write), and two
+    read-only streams -- the ceiling for kernels that only read, like decode:
+    a bf16 matrix-vector product through torch (reads the [read_rows, n]
+    matrix once, writes read_rows values) and torch's sum over a fp32 buffer
+    of the same size (reads every byte once, writes one value).  The faster
+    of the two is the read ceiling."""
     a = torch.randn((n, n), device=dev).to(torch.bfloat16)
     b = torch.randn((n, n), device=dev).to(torch.bfloat16)
     c = a @ b
     src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     dst.copy_(src)
+    mat = torch.empty((read_rows, n), dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
+    vec = torch.empty((n, 1), dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
+    y = mat @ vec
+    read_bytes = mat.numel() * mat.element_size()
     rd = torch.ones(read_bytes // 4, dtype=torch.float32, device=dev)
     acc = torch.empty((), dtype=torch.float32, device=dev)
     torch.sum(rd, dim=0, out=acc)
     torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     e[0].record()
     for _ in range(reps):
         torch.matmul(a, b, out=c)
@@ -305,19 +312,27 @@ def reference_rates(dev="cuda:0", n=16384, copy_bytes=1 << 30, read_bytes=1 << 3
         dst.copy_(src)
     e[2].record()
     for _ in range(reps):
-        torch.sum(rd, dim=0, out=acc)
+        torch.matmul(mat, vec, out=y)
     e[3].record()
+    for _ in range(reps):
+        torch.sum(rd, dim=0, out=acc)
+    e[4].record()
     torch.cuda.synchronize()
     gemm_ms = e[0].elapsed_time(e[1]) / reps
     copy_ms = e[1].elapsed_time(e[2]) / reps
-    read_ms = e[2].elapsed_time(e[3]) / reps
-    del a, b, c, src, dst, rd, acc
+    gemv_ms = e[2].elapsed_time(e[3]) / reps
+    sum_ms = e[3].elapsed_time(e[4]) / reps
+    del a, b, c, src, dst, mat, vec, y, rd, acc
     torch.cuda.empty_cache()
+    gemv_gbs = read_bytes / (gemv_ms * 1e-3) / 1e9
+    sum_gbs = read_bytes / (sum_ms * 1e-3) / 1e9
     return {"bf16_gemm_TFLOP_per_s": 2.0 * n ** 3 / (gemm_ms * 1e-3) / 1e12, "gemm_shape": f"{n}x{n}x{n}",
             "d2d_copy_GB_per_s": 2.0 * copy_bytes / (copy_ms * 1e-3) / 1e9,
             "copy_bytes": copy_bytes, "copy_note": "read + write bytes per copy",
-            "read_only_GB_per_s": read_bytes / (read_ms * 1e-3) / 1e9, "read_bytes": read_bytes,
-            "read_note": "torch.sum over a fp32 buffer: bytes read per pass"}
+            "read_only_GB_per_s": max(gemv_gbs, sum_gbs), "read_bytes": read_bytes,
+            "gemv_read_GB_per_s": gemv_gbs, "sum_read_GB_per_s": sum_gbs,
+            "read_note": f"faster of a bf16 [{read_rows}x{n}] matrix-vector product and a fp32 sum, "
+                         "bytes read per pass"}
 
 
 def bench_decode(cca, cfg, steps_timed=True):

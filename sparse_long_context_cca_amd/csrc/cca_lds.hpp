@@ -19,6 +19,7 @@ namespace cca {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -31,17 +32,20 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef std::integral_constant<bool, true> CoreTile;   // fp16 operands
 typedef std::integral_constant<bool, false> RawTile;   // bf16 operands
 
-template <bool F16>
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+// The B operand may also come typed as f16x8 (no reinterpretation).
+__device__ __forceinline__ f16x8 as_f16(const bf16x8& x) { return __builtin_bit_cast(f16x8, x); }
+__device__ __forceinline__ f16x8 as_f16(const f16x8& x) { return x; }
+template <bool F16, class BT>
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const BT& b, const f32x16& c) {
   if constexpr (F16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16(a), as_f16(b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-template <bool F16>
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+template <bool F16, class BT>
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const BT& b, const f32x4& c) {
   if constexpr (F16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16(a), as_f16(b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

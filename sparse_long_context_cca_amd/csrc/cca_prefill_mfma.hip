@@ -11,18 +11,16 @@
 //     owns 32 rows (one head, 32 consecutive positions).  With GQA several
 //     waves are query heads at the same positions, and every K/V tile staged
 //     in LDS serves all eight waves.
-//   * The workgroup walks the union of its rows' visible keys: first the core
-//     tiles 0..n_core(last row) (64 cores each), then the raw tiles covering
-//     win_lo(first row)..last row (64 positions each, 64-aligned).  Tiles
-//     that every row of a wave sees completely skip the mask; tiles no row of
-//     a wave sees are fully masked.
-//   * The cores are stored in fp16 (three more mantissa bits than bf16: a
-//     core is a weighted mean of keys that can be large), so core tiles run
-//     on fp16 MFMAs with the Q fragments converted to fp16 in registers and
-//     the probabilities rounded to fp16; raw tiles run on bf16 MFMAs (the
-//     inputs' dtype) with Q converted back (the round trip returns every
-//     |q| >= 2^-17 exactly, smaller ones within 2^-25).  Cores first: in a
-//     same-process comparison the other order ran 2% slower.
+//   * The workgroup walks the union of its rows' visible keys: first the raw
+//     tiles covering win_lo(first row)..last row (64 positions each,
+//     64-aligned), then the core tiles 0..n_core(last row) (64 cores each).
+//     Tiles that every row of a wave sees completely skip the mask; tiles no
+//     row of a wave sees are fully masked.
+//   * Raw tiles run on bf16 MFMAs (the inputs' dtype).  The cores are stored
+//     in fp16 (three more mantissa bits than bf16: a core is a weighted mean
+//     of keys that can be large), so core tiles run on fp16 MFMAs: when the
+//     walk reaches them, each wave converts its Q fragments to fp16 once, in
+//     registers, and the probabilities of core tiles are rounded to fp16.
 //   * Workgroups are issued longest-first (the last positions see the most
 //     cores) and, when the kv heads divide evenly over the 8 XCDs, all
 //     workgroups of one kv head run on one XCD so that its core K/V stay in
@@ -165,7 +163,7 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int wnc_lo = uni(n_core(w_lo, g, w));
   const int wlo_hi = uni(win_lo(w_hi, w));
 
-  // ---- workgroup key range: core tiles 0 .. n_ct-1, then raw tiles
+  // ---- workgroup key range: raw tiles 0 .. n_rt-1, then core tiles
   const int nc_hi = uni(n_core(P_hi, g, w));
   const int n_ct = uni((nc_hi + kBK - 1) / kBK);
   const int raw_lo = win_lo(P_lo, w);
@@ -217,8 +215,8 @@ void prefill_mfma_kernel(PrefillParams P) {
     voff[i] = row * D * 2 + ((pos ^ vswz(row)) * 4 + sub) * 16;
   }
 
-  auto tile_core = [&](int it) { return it < n_ct; };
-  auto tile_base = [&](int it) { return it < n_ct ? it * kBK : r0 + (it - n_ct) * kBK; };
+  auto tile_core = [&](int it) { return it >= n_rt; };
+  auto tile_base = [&](int it) { return it >= n_rt ? (it - n_rt) * kBK : r0 + it * kBK; };
   auto rsrc = [&](int it, bool values) {
     const bool core = tile_core(it);
     const int base = tile_base(it);
@@ -278,19 +276,23 @@ void prefill_mfma_kernel(PrefillParams P) {
   // c+16 and c+48 (query row c+16).  Lane c < 16 holds C[0][c] and C[1][c]
   // in lsum[0] and lsum[1]; the other rows of C stay zero.
   f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-  // the selector in both operand types (the transition tile sums a raw tile's
-  // bf16 probabilities while its own are fp16)
+  // The selector holds ones in the operand type of the probabilities it sums:
+  // bf16 through the raw tiles, fp16 through the core tiles.
   const bool sel_on = lane == 0 || lane == 32 || lane == 17 || lane == 49;
-  bf16x8 sel_bf, sel_h;
-  {
-    f16x8 s16;
+  auto selector = [&](auto core_tag) {
+    bf16x8 s;
+    if constexpr (decltype(core_tag)::value) {
+      f16x8 h;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sel_bf[e] = static_cast<__bf16>(sel_on ? 1.0f : 0.0f);
-      s16[e] = static_cast<_Float16>(sel_on ? 1.0f : 0.0f);
+      for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(sel_on ? 1.0f : 0.0f);
+      s = __builtin_bit_cast(bf16x8, h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] = static_cast<__bf16>(sel_on ? 1.0f : 0.0f);
     }
-    sel_h = __builtin_bit_cast(bf16x8, s16);
-  }
+    return s;
+  };
+  bf16x8 sel = selector(RawTile{});
   // rescale the row sums by their rows' factors (lane c < 16 needs those of
   // rows c and c+16, held by lanes c and c+16)
   auto rescale_sums = [&](float a) {
@@ -317,12 +319,10 @@ void prefill_mfma_kernel(PrefillParams P) {
   for (int i = tid; i < VBytes / 16; i += kThreads)
     *reinterpret_cast<u32x4*>(vbuf(2) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NKMIN + NVW) : "memory");
-  // probabilities of the previous tile (zeros before the first), bf16 B operands
+  // probabilities of the previous tile, the B operands of its P.V: bf16 for
+  // a raw tile (pr), fp16 for a core tile (prh); each walk starts them at zero
   bf16x8 pr[4];
-#pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pr[cc][e] = static_cast<__bf16>(0.0f);
+  f16x8 prh[4];
 
   // Iteration it: LDS holds K(it) (K slot it%3) and V(it-1) (V slot
   // (it+2)%3); K(it+1) and V(it) are landing.  It issues the loads of K(it+2)
@@ -414,23 +414,36 @@ void prefill_mfma_kernel(PrefillParams P) {
     ring[1] = vfrag(1);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      u32x4 pnew;
+      // the new chunk is built element-wise in its own type (vector bit-casts
+      // of packed dwords here made the compiler copy the fragments around)
+      bf16x8 pnew;
+      f16x8 pnew_h;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int n = cc * DB + db;
         if (n + 2 < NPV) ring[(n + 2) % 3] = vfrag(n + 2);
-        o[db] = mfma32<PREV>(ring[n % 3], pr[cc], o[db]);
+        if constexpr (PREV) o[db] = mfma32<true>(ring[n % 3], prh[cc], o[db]);
+        else o[db] = mfma32<false>(ring[n % 3], pr[cc], o[db]);
 #pragma unroll
         for (int e = db * PPM; e < db * PPM + PPM; e += 2) {
           const int r = (cc & 1) * 8 + e;
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r], c, -mc));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sx[cc >> 1][r + 1], c, -mc));
-          pnew[e >> 1] = pack_op<CUR>(p0, p1);
+          if constexpr (CUR) {
+            pnew_h[e] = static_cast<_Float16>(p0);
+            pnew_h[e + 1] = static_cast<_Float16>(p1);
+          } else {
+            pnew[e] = static_cast<__bf16>(p0);
+            pnew[e + 1] = static_cast<__bf16>(p1);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      lsum = mfma16<PREV>(PREV ? sel_h : sel_bf, pr[cc], lsum);  // tile it-1's chunk cc, then replaced by tile it's
-      pr[cc] = __builtin_bit_cast(bf16x8, pnew);
+      // tile it-1's chunk cc into the row sums, then replaced by tile it's
+      if constexpr (PREV) lsum = mfma16<true>(sel, prh[cc], lsum);
+      else lsum = mfma16<false>(sel, pr[cc], lsum);
+      if constexpr (CUR) prh[cc] = pnew_h;
+      else pr[cc] = pnew;
     }
     grow_pending = __builtin_amdgcn_ballot_w64(grow) != 0;
     alpha_pending = alpha;
@@ -439,37 +452,63 @@ void prefill_mfma_kernel(PrefillParams P) {
   };
   // core tiles on fp16 Q fragments, then the raw tiles on bf16 ones ("tile
   // -1" holds zero probabilities, which read the same in either type)
-  int it = 0;
-  if (n_ct > 0) {
+  auto apply_pending_rescale = [&]() {
+    if (grow_pending) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16_frag_to_f16(qf[ks]);
-    for (; it < n_ct; ++it) iteration(it, CoreTile{}, CoreTile{});
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = f16_frag_to_bf16(qf[ks]);
-    iteration(it++, RawTile{}, CoreTile{});
-  }
-  for (; it < n_tiles; ++it) iteration(it, RawTile{}, RawTile{});
-  // the loads issued for tiles past the end must land before the workgroup's
-  // LDS can be handed to another
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (grow_pending) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
-    rescale_sums(alpha_pending);
-  }
-  auto last_tile = [&](auto core_tag) {
-    constexpr bool LAST = decltype(core_tag)::value;
-    const char* vt = vbuf(kslot == 0 ? 2 : kslot - 1);  // V(n_tiles - 1)
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
+      rescale_sums(alpha_pending);
+    }
+    grow_pending = false;
+  };
+  // The P.V of a walk's last tile, outside the pipeline: V(last) sits in the
+  // V slot before the next load slot.
+  auto flush_tile = [&](auto core_tag) {
+    constexpr bool CORE = decltype(core_tag)::value;
+    apply_pending_rescale();
+    const char* vt = vbuf(kslot == 0 ? 2 : kslot - 1);
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = mfma32<LAST>(vfrag_at(vt, cc, db), pr[cc], o[db]);
+      for (int db = 0; db < DB; ++db) {
+        if constexpr (CORE) o[db] = mfma32<true>(vfrag_at(vt, cc, db), prh[cc], o[db]);
+        else o[db] = mfma32<false>(vfrag_at(vt, cc, db), pr[cc], o[db]);
+      }
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) lsum = mfma16<LAST>(LAST ? sel_h : sel_bf, pr[cc], lsum);
+    for (int cc = 0; cc < 4; ++cc) {
+      if constexpr (CORE) lsum = mfma16<true>(sel, prh[cc], lsum);
+      else lsum = mfma16<false>(sel, pr[cc], lsum);
+    }
   };
-  last_tile(RawTile{});  // the walk always ends on a raw tile (every row sees itself)
+  // Raw tiles on bf16 Q fragments, then the core tiles on fp16 ones (converted
+  // once, in registers; no value goes back).  Each walk starts with zero
+  // probabilities standing for "tile -1" (whose V slot holds finite values),
+  // and the raw walk ends with its last tile's P.V flushed.  In a
+  // same-process comparison this order and the flush ran faster than the
+  // core walk first with a transition tile, whose loop carried 16 register
+  // copies of the probabilities per tile.
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[cc][e] = static_cast<__bf16>(0.0f);
+  for (int it = 0; it < n_rt; ++it) iteration(it, RawTile{}, RawTile{});
+  if (n_ct > 0) {
+    flush_tile(RawTile{});
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16_frag_to_f16(qf[ks]);
+    sel = selector(CoreTile{});
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) prh[cc][e] = static_cast<_Float16>(0.0f);
+    for (int it = n_rt; it < n_tiles; ++it) iteration(it, CoreTile{}, CoreTile{});
+  }
+  // the loads issued for tiles past the end must land before the workgroup's
+  // LDS can be handed to another
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (n_ct > 0) flush_tile(CoreTile{});  // the walk's last tile
+  else flush_tile(RawTile{});
 
   // ---- normalise and store: lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
   // row j's sum: lane j%16 holds it, in lsum[0] for j < 16 and lsum[1] above
