@@ -193,6 +193,8 @@ def bench_prefill(cca, cfg, steps, warmup, inputs=None):
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        if ev is not None:
+            ev[2].record(stream)
         cca.cca_pool_core(qd, kd, vd, ck, cv, cfg.g)
         if ev is not None:
             ev[0].record(stream)
@@ -203,7 +205,8 @@ def bench_prefill(cca, cfg, steps, warmup, inputs=None):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # per step: prefill start (= pooling end), prefill end, pooling start
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(steps):
@@ -211,10 +214,11 @@ def bench_prefill(cca, cfg, steps, warmup, inputs=None):
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    prefill_ms = [a.elapsed_time(b) for a, b in evs]
+    prefill_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    pool_each = [e[2].elapsed_time(e[0]) for e in evs]
     ms_step = total_ms / steps
     prefill_avg = sum(prefill_ms) / len(prefill_ms)
-    pool_ms = ms_step - prefill_avg
+    pool_ms = sum(pool_each) / len(pool_each)
     assert torch.isfinite(out[0, :, -4:].float()).all()
     flops = prefill_flops(cfg)
     tflops = flops / (prefill_avg * 1e-3) / 1e12

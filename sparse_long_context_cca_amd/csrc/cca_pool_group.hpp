@@ -29,13 +29,16 @@ enum PoolMode { kPoolSoftmax = 0, kPoolSoftmaxHeads = 1, kPoolMean = 2, kPoolMax
 constexpr int kPoolHeadsMaxG = 8;  // kPoolSoftmaxHeads keeps one state per head in registers
 
 template <int DT>
-struct Row16;  // a lane's 16-byte slice of a row, as floats
+struct Row16;  // a lane's 16-byte slice of a row, as floats (unpack: from its raw bits)
 template <>
 struct Row16<0> {
   static constexpr int N = 4;
+  static __device__ __forceinline__ void unpack(const uint4& v, float* x) {
+    x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+  }
   static __device__ __forceinline__ void load(const void* p, float* x) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    unpack(*reinterpret_cast<const uint4*>(p), x);
   }
   static __device__ __forceinline__ void store(void* p, const float* x) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
@@ -44,14 +47,16 @@ struct Row16<0> {
 template <>
 struct Row16<1> {
   static constexpr int N = 8;
-  static __device__ __forceinline__ void load(const void* p, float* x) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
+  static __device__ __forceinline__ void unpack(const uint4& v, float* x) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[2 * i] = __uint_as_float(w[i] << 16);
       x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
+  }
+  static __device__ __forceinline__ void load(const void* p, float* x) {
+    unpack(*reinterpret_cast<const uint4*>(p), x);
   }
   static __device__ __forceinline__ void store(void* p, const float* x) {
     uint4 v;
@@ -66,14 +71,16 @@ struct Row16<1> {
 template <>
 struct Row16<2> {  // fp16 (the core cache of bf16 inputs)
   static constexpr int N = 8;
-  static __device__ __forceinline__ void load(const void* p, float* x) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
+  static __device__ __forceinline__ void unpack(const uint4& v, float* x) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[2 * i] = f16_to_f32((uint16_t)(w[i] & 0xffffu));
       x[2 * i + 1] = f16_to_f32((uint16_t)(w[i] >> 16));
     }
+  }
+  static __device__ __forceinline__ void load(const void* p, float* x) {
+    unpack(*reinterpret_cast<const uint4*>(p), x);
   }
   static __device__ __forceinline__ void store(void* p, const float* x) {
     uint4 v;
@@ -187,6 +194,22 @@ __device__ __forceinline__ void pool_group(KRow krow, VRow vrow, QRow qrow, int 
         for (int tau = 0; tau < g; ++tau) wout[tau] = inv;
     }
   } else if constexpr (MODE == kPoolSoftmax) {
+    // The group's rows are read one round ahead of their use (raw 16-byte
+    // slices), and the first round is requested before the query rows.  In
+    // one process on one MI355X this took the GQA 128K pooling from 126-132
+    // to 122-124 us; four rounds ahead (a group of 16 in flight at once)
+    // took 155 us, its registers costing a wave per SIMD.
+    auto fetch = [&](int c0, uint4& kr, uint4& vr) {
+      const int tau = c0 + ks;
+      if (tau < g) {
+        kr = *reinterpret_cast<const uint4*>(krow(tau) + off);
+        vr = *reinterpret_cast<const uint4*>(vrow(tau) + off);
+      } else {
+        kr = vr = make_uint4(0u, 0u, 0u, 0u);
+      }
+    };
+    uint4 kr, vr;
+    fetch(0, kr, vr);
     // pooling query: mean over the G heads of the last-token queries
     float qbar[EPL];
 #pragma unroll
@@ -209,13 +232,9 @@ __device__ __forceinline__ void pool_group(KRow krow, VRow vrow, QRow qrow, int 
       const int tau = c0 + ks;
       const bool valid = tau < g;
       float kx[EPL], vx[EPL];
-      if (valid) {
-        R16::load(krow(tau) + off, kx);
-        R16::load(vrow(tau) + off, vx);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) kx[e] = vx[e] = 0.f;
-      }
+      R16::unpack(kr, kx);  // zeros past the group
+      R16::unpack(vr, vx);
+      if (c0 + RL::KPW < g) fetch(c0 + RL::KPW, kr, vr);
       const float part = row_dot<DT, D>(qbar, kx);
       const float s = valid ? part * scale_log2 : -INFINITY;  // log2-domain score
       const float mnew = fmaxf(m, s);
