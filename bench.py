@@ -129,7 +129,9 @@ def cpu_oracle_baseline(cfg, q, k, v, budget_s=20.0):
     """Times the fp64 CPU oracle (as it stands) on a bounded sample of the
     prefill workload: pooling of one kv head over all L tokens (scaled to all
     kv heads) plus the attention rows of the last S positions for every query
-    head; S doubles until the sample costs about budget_s/2."""
+    head; S doubles until one sample costs more than budget_s/4, so the timed
+    (last) sample takes budget_s/4 to budget_s/2 and all samples together
+    about twice that."""
     import oracle.cca_oracle as orc
     try:
         from threadpoolctl import threadpool_limits
