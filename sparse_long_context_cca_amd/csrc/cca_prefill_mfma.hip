@@ -450,8 +450,8 @@ void prefill_mfma_kernel(PrefillParams P) {
     kslot = next;
     sync_stage();
   };
-  // core tiles on fp16 Q fragments, then the raw tiles on bf16 ones ("tile
-  // -1" holds zero probabilities, which read the same in either type)
+  // the rescale the last tile's new max asked for, before a P.V that runs
+  // outside the pipeline
   auto apply_pending_rescale = [&]() {
     if (grow_pending) {
 #pragma unroll
