@@ -92,6 +92,8 @@ BWD_CASES = [
     ("bf16", 2, 16, 8, 200, 128, 16, 64, cca.CCA_POOL_SOFTMAX),  # B * Hkv = 16: 2 kv heads per XCD
     ("bf16", 1, 2, 1, 1, 128, 16, 4, cca.CCA_POOL_SOFTMAX),      # L = 1
     ("bf16", 1, 4, 2, 40, 128, 64, 8, cca.CCA_POOL_MAX),         # g > L: no core at all
+    ("bf16", 1, 8, 2, 3000, 64, 16, 128, cca.CCA_POOL_SOFTMAX),  # d = 64: several core blocks
+    ("f32", 1, 4, 1, 1500, 64, 16, 64, cca.CCA_POOL_SOFTMAX),    # d = 64 on the vector ALUs, longer
 ]
 
 

@@ -186,6 +186,8 @@ PREFILL_CASES = [
     (1, 4, 2, 1300, 128, 100, 150),   # g = 100
     (1, 16, 16, 700, 64, 16, 64),     # 16 kv heads: two per XCD, run one after the other
     (2, 32, 16, 600, 128, 16, 128),   # 32 (batch, kv head) units: four per XCD across the batch
+    (1, 8, 2, 6000, 64, 16, 256),     # d = 64, G = 4: eight core tiles, a ragged last block
+    (2, 4, 4, 3500, 64, 8, 100),      # d = 64, one query head per kv head, g = 8
 ]
 
 
