@@ -43,6 +43,10 @@
 // Online softmax in the log2 domain with fp32 state and a lazy rescale.  K
 // and V tiles are loaded straight from memory into three-slot LDS rings, two
 // tiles ahead (buffer loads whose range check zero-fills keys past the end).
+#include <algorithm>
+#include <atomic>
+#include <mutex>
+
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
 #include "cca_lds.hpp"
@@ -67,8 +71,30 @@ struct PrefillParams {
   int G, Hw, RP;        // heads per workgroup, rows per head per workgroup
   int nPB, nHG, U;      // position blocks, head groups per kv head, units
   int xcd;              // 1 when units split evenly over 8 XCDs
+  int total;            // items (a workgroup's worth of rows each): nPB * U
+  int n_static;         // items 0 .. n_static-1 go one to a workgroup, in block order
+  int qslot;            // work-queue slot of this launch (for the items after them)
   float c;              // softmax scale * log2(e)
 };
+
+// The kernel's arguments, read afresh from the kernarg segment: the empty asm
+// hides the pointer's value, so the loads through it stay where they are
+// written (the kernel runs its item code in two places, and arguments
+// hoisted out of both would stay live across the tile loops and spill).
+typedef const __attribute__((address_space(4))) PrefillParams* ArgPtr;
+__device__ __forceinline__ ArgPtr kernel_args() {
+  const __attribute__((address_space(4))) char* p =
+      (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return reinterpret_cast<ArgPtr>(p);
+}
+
+// Work queues of the items that are not given out by block id: one slot per
+// launch in flight; words 0..7 count the positions taken from the eight
+// per-XCD queues, word 8 the queue workgroups that have finished.  The last
+// of those clears the slot (device memory starts zeroed).
+constexpr int kQueueSlots = 64;
+__device__ unsigned g_prefill_queue[kQueueSlots * 16];
 
 // Lanes l and l^32 hold the two halves of one query row's scores.  One
 // v_permlane32_swap of a register with itself leaves {x[l], x[l^32]} in the
@@ -109,44 +135,48 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int j = lane & 31;
   const int hh = lane >> 5;
 
-  // ---- which rows: longest first, XCD-aware.  Block ids are dealt round
+  // One item: the rows of one workgroup, start to end (the LDS rings are
+  // idle again when it returns).
+  auto item_body = [&](const long bid) {
+  const ArgPtr A = kernel_args();
+  // ---- which rows: longest first, XCD-aware.  Item ids are dealt round
   // robin over the XCDs; on XCD x the slots walk unit x*per's position blocks
   // from the last down, then unit x*per+1's, and so on.
-  const long bid = blockIdx.x;
   int pb, u;
-  if (P.xcd) {
-    const int per = P.U / 8;
+  if (A->xcd) {
+    const int per = A->U / 8;
     const long slot = bid >> 3;
     const int x = (int)(bid & 7);
-    pb = P.nPB - 1 - (int)(slot % P.nPB);
-    u = x * per + (int)(slot / P.nPB);
+    pb = A->nPB - 1 - (int)(slot % A->nPB);
+    u = x * per + (int)(slot / A->nPB);
   } else {
-    pb = P.nPB - 1 - (int)(bid / P.U);
-    u = (int)(bid % P.U);
+    pb = A->nPB - 1 - (int)(bid / A->U);
+    u = (int)(bid % A->U);
   }
-  const int kvp = u / P.nHG;  // b * Hkv + kv head
-  const int hg = u % P.nHG;
-  const int b = kvp / P.Hkv;
-  const int kvh = kvp % P.Hkv;
-  const int g = P.g, w = P.w;
-  const int h = kvh * P.G + hg * P.Hw + (wave % P.Hw);
-  const int row0 = pb * P.RP + 32 * (wave / P.Hw);  // local row of the wave's first row
+  const int kvp = u / A->nHG;  // b * Hkv + kv head
+  const int hg = u % A->nHG;
+  const int b = kvp / A->Hkv;
+  const int kvh = kvp % A->Hkv;
+  const int g = A->g, w = A->w;
+  const int h = kvh * A->G + hg * A->Hw + (wave % A->Hw);
+  const int row0 = pb * A->RP + 32 * (wave / A->Hw);  // local row of the wave's first row
   // sequence b's rows: positions qs .. qs + ql - 1 at local rows 0 .. ql - 1
-  const SeqRows sr = seq_rows(P.q_start, P.q_len, b, P.Lq, P.Lk, g, w, P.m_cap);
+  const SeqRows sr = seq_rows(A->q_start, A->q_len, b, A->Lq, A->Lk, g, w, A->m_cap);
   if (!sr.ok) {  // rows that do not fit the buffers: NaN, nothing read
-    if (row0 + j < P.Lq) {
-      const long orow = (((long)b * P.Hq + h) * P.Lq + row0 + j) * D;
+    if (row0 + j < A->Lq) {
+      const long orow = (((long)b * A->Hq + h) * A->Lq + row0 + j) * D;
+#pragma unroll 1
       for (int e = hh; e < D; e += 2) {
-        if (OT == 1) static_cast<uint16_t*>(P.out)[orow + e] = 0x7fc0;
-        else static_cast<float*>(P.out)[orow + e] = NAN;
+        if (OT == 1) static_cast<uint16_t*>(A->out)[orow + e] = 0x7fc0;
+        else static_cast<float*>(A->out)[orow + e] = NAN;
       }
     }
     return;
   }
   const int qs = sr.qs, Le = sr.qs + sr.ql;  // first position, one past the last
-  if (pb * P.RP >= sr.ql) return;             // the whole workgroup lies past the end
-  const int P_lo = qs + pb * P.RP;
-  const int P_hi = min(Le - 1, P_lo + P.RP - 1);
+  if (pb * A->RP >= sr.ql) return;             // the whole workgroup lies past the end
+  const int P_lo = qs + pb * A->RP;
+  const int P_hi = min(Le - 1, P_lo + A->RP - 1);
   const int p0 = qs + row0;
 
   // ---- this lane's query row and the wave's row range
@@ -172,15 +202,15 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int n_tiles = uni(n_ct + n_rt);
 
   const long kvrow = (long)kvp;
-  const uint16_t* kbase = P.k + kvrow * P.Lk * D;
-  const uint16_t* vbase = P.v + kvrow * P.Lk * D;
-  const uint16_t* ckbase = P.ck + kvrow * P.m_cap * D;
-  const uint16_t* cvbase = P.cv + kvrow * P.m_cap * D;
+  const uint16_t* kbase = A->k + kvrow * A->Lk * D;
+  const uint16_t* vbase = A->v + kvrow * A->Lk * D;
+  const uint16_t* ckbase = A->ck + kvrow * A->m_cap * D;
+  const uint16_t* cvbase = A->cv + kvrow * A->m_cap * D;
 
   // ---- Q fragment: B operand, lane holds Q[row j][16ks + 8hh .. +7]
   bf16x8 qf[KS];
   {
-    const uint16_t* qrow = P.q + (((long)b * P.Hq + h) * P.Lq + (t - qs)) * D;
+    const uint16_t* qrow = A->q + (((long)b * A->Hq + h) * A->Lq + (t - qs)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hh);
     // Use the fragments here, so that the compiler waits for these loads now:
@@ -300,7 +330,7 @@ void prefill_mfma_kernel(PrefillParams P) {
     lsum[0] *= a;
     lsum[1] *= a_hi;
   };
-  const float c = P.c;
+  const float c = A->c;
 
   // End of a pipeline stage: this wave's loads of the previous stage (K(it+1),
   // V(it)) have landed in LDS, then the workgroup meets.  Loads finish in
@@ -374,12 +404,16 @@ void prefill_mfma_kernel(PrefillParams P) {
       const int lo_rel = CUR ? 0 : my_lo - base;
       const int hi_rel = CUR ? my_nc - 1 - base : t - base;
       const unsigned span = (unsigned)(hi_rel - lo_rel);
+      // key offsets from one per-lane value made here (hidden from the
+      // compiler, which would otherwise keep all 32 live across the loop)
+      int off = 4 * hh - lo_rel;
+      asm volatile("" : "+v"(off));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool vis = hi_rel >= lo_rel && (unsigned)(kk - lo_rel) <= span;
+          const int kk = 32 * kb + 8 * (r >> 2) + (r & 3);
+          const bool vis = hi_rel >= lo_rel && (unsigned)(kk + off) <= span;
           sx[kb][r] = vis ? sx[kb][r] : -INFINITY;
         }
     }
@@ -517,7 +551,7 @@ void prefill_mfma_kernel(PrefillParams P) {
   const float ltot = j < 16 ? l_lo : l_hi;
   const float inv = 1.0f / ltot;
   if (t_raw < Le) {
-    const long orow = (((long)b * P.Hq + h) * P.Lq + (t_raw - qs)) * D;
+    const long orow = (((long)b * A->Hq + h) * A->Lq + (t_raw - qs)) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -526,21 +560,85 @@ void prefill_mfma_kernel(PrefillParams P) {
         const float x0 = o[db][4 * rr + 0] * inv, x1 = o[db][4 * rr + 1] * inv;
         const float x2 = o[db][4 * rr + 2] * inv, x3 = o[db][4 * rr + 3] * inv;
         if (OT == 1) {
-          uint16_t* out = static_cast<uint16_t*>(P.out);
+          uint16_t* out = static_cast<uint16_t*>(A->out);
           *reinterpret_cast<uint2*>(out + orow + d0) = make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
         } else {
-          float* out = static_cast<float*>(P.out);
+          float* out = static_cast<float*>(A->out);
           *reinterpret_cast<float4*>(out + orow + d0) = make_float4(x0, x1, x2, x3);
         }
       }
     // the softmax's normaliser for a backward pass: probabilities are
     // exp2(s c - m c) / ltot, so log-sum-exp (natural log) = (m c + log2 ltot) ln 2
-    if (P.lse != nullptr && hh == 0)
-      P.lse[((long)b * P.Hq + h) * P.Lq + (t_raw - qs)] = (m * c + log2f(ltot)) * kLn2;
+    if (A->lse != nullptr && hh == 0)
+      A->lse[((long)b * A->Hq + h) * A->Lq + (t_raw - qs)] = (m * c + log2f(ltot)) * kLn2;
+  }
+  };
+
+  // ---- blocks below n_static run item blockIdx.x.  The others (dispatched
+  // last, one per compute unit) take the remaining items, the shortest, from
+  // eight per-XCD queues: their own XCD's first, then the others' in turn, so
+  // that an XCD that runs faster ends up with more of them and the XCDs finish
+  // together.  Lane 0 of wave 0 talks to the queues; the item reaches the
+  // other waves through LDS.
+  if ((int)blockIdx.x < P.n_static) {
+    item_body(blockIdx.x);
+    return;
+  }
+  unsigned* const queue = g_prefill_queue + 16 * P.qslot;
+  __shared__ int claimed;
+  int cq = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7u);  // XCC id
+  int dead = 0;  // queues found empty
+  const int n_tail = P.total - P.n_static;
+  for (;;) {
+    if (tid == 0) {
+      int i = -1;
+      while (dead < 8) {
+        const unsigned s = __hip_atomic_fetch_add(queue + cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const long pos = cq + 8L * s;  // queue x holds tail items x, x + 8, ...
+        if (pos < n_tail) {
+          i = P.n_static + (int)pos;
+          break;
+        }
+        cq = (cq + 1) & 7;
+        ++dead;
+      }
+      claimed = i;
+    }
+    __syncthreads();  // also: every wave is done with the previous item's LDS
+    const int item = __builtin_amdgcn_readfirstlane(claimed);
+    __syncthreads();  // every wave has read it before it is written again
+    if (item < 0) break;
+    item_body(item);
+  }
+  if (tid == 0) {
+    const unsigned done = __hip_atomic_fetch_add(queue + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == gridDim.x - P.n_static - 1) {
+      for (int x = 0; x < 9; ++x) __hip_atomic_store(queue + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
 constexpr int kWaves = 8;  // waves per workgroup
+
+// Compute units of the current device, looked up once per device.
+hipError_t compute_units(int* out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int counts[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (counts[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    counts[dev] = n > 0 ? n : 1;
+  }
+  *out = counts[dev];
+  return hipSuccess;
+}
 
 int gcd_int(int a, int b) {
   while (b) {
@@ -582,8 +680,21 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
   P.U = sh.B * sh.Hkv * P.nHG;
   P.xcd = (P.U % 8 == 0) ? 1 : 0;
   P.c = kLog2e / sqrtf((float)sh.d);
-  const long blocks = (long)P.nPB * P.U;
-  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  const long items = (long)P.nPB * P.U;
+  if (items > 0x7fffffffL / 2) return hipErrorInvalidConfiguration;
+  if (items == 0) return hipSuccess;
+  P.total = (int)items;
+  // The shortest quarter of the items (a multiple of 8, so that each keeps
+  // its XCD) goes to one queue workgroup per compute unit, when there are
+  // enough items for the XCDs to drift apart.
+  int cus = 0;
+  const hipError_t ce = compute_units(&cus);
+  if (ce != hipSuccess) return ce;
+  const int n_tail = items >= 8L * cus ? (int)(items / 4) & ~7 : 0;
+  P.n_static = P.total - n_tail;
+  const long blocks = (long)P.n_static + std::min(n_tail, cus);
+  static std::atomic<unsigned> launches{0};
+  P.qslot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
   if (sh.d == 64) {
     if (out_dt == 1) hipLaunchKernelGGL((prefill_mfma_kernel<64, 1, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
     else hipLaunchKernelGGL((prefill_mfma_kernel<64, 0, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
