@@ -5,12 +5,36 @@
 
 #include <cstdio>
 #include <cstdarg>
+#include <mutex>
 #include <string>
 
 #include "../../include/cca.h"
 #include "cca_device.hpp"
 #include "cca_pool_group.hpp"
 #include "cca_internal.hpp"
+
+namespace cca {
+
+hipError_t compute_units(int* out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int counts[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (counts[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    counts[dev] = n > 0 ? n : 1;
+  }
+  *out = counts[dev];
+  return hipSuccess;
+}
+
+}  // namespace cca
 
 namespace {
 

@@ -49,6 +49,9 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
                                const void* cv, int m_cap, void* out, int out_dt, const Shape& sh,
                                const RowRange& rr, float* lse, hipStream_t s);
 
+// Compute units of the current device (looked up once per device).
+hipError_t compute_units(int* out);
+
 struct DecodePlan {
   int splits;         // key-range splits per (b, kv head)
   size_t ws_bytes;    // workspace bytes

@@ -50,6 +50,7 @@
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
 #include "cca_lds.hpp"
+#include "cca_queue.hpp"
 
 namespace cca {
 namespace {
@@ -77,23 +78,7 @@ struct PrefillParams {
   float c;              // softmax scale * log2(e)
 };
 
-// The kernel's arguments, read afresh from the kernarg segment: the empty asm
-// hides the pointer's value, so the loads through it stay where they are
-// written (the kernel runs its item code in two places, and arguments
-// hoisted out of both would stay live across the tile loops and spill).
-typedef const __attribute__((address_space(4))) PrefillParams* ArgPtr;
-__device__ __forceinline__ ArgPtr kernel_args() {
-  const __attribute__((address_space(4))) char* p =
-      (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(p));
-  return reinterpret_cast<ArgPtr>(p);
-}
-
-// Work queues of the items that are not given out by block id: one slot per
-// launch in flight; words 0..7 count the positions taken from the eight
-// per-XCD queues, word 8 the queue workgroups that have finished.  The last
-// of those clears the slot (device memory starts zeroed).
-constexpr int kQueueSlots = 64;
+// the tail queues' counters (cca_queue.hpp)
 __device__ unsigned g_prefill_queue[kQueueSlots * 16];
 
 // Lanes l and l^32 hold the two halves of one query row's scores.  One
@@ -138,7 +123,7 @@ void prefill_mfma_kernel(PrefillParams P) {
   // One item: the rows of one workgroup, start to end (the LDS rings are
   // idle again when it returns).
   auto item_body = [&](const long bid) {
-  const ArgPtr A = kernel_args();
+  const auto* const A = kernel_args<PrefillParams>();
   // ---- which rows: longest first, XCD-aware.  Item ids are dealt round
   // robin over the XCDs; on XCD x the slots walk unit x*per's position blocks
   // from the last down, then unit x*per+1's, and so on.
@@ -574,71 +559,27 @@ void prefill_mfma_kernel(PrefillParams P) {
   }
   };
 
-  // ---- blocks below n_static run item blockIdx.x.  The others (dispatched
-  // last, one per compute unit) take the remaining items, the shortest, from
-  // eight per-XCD queues: their own XCD's first, then the others' in turn, so
-  // that an XCD that runs faster ends up with more of them and the XCDs finish
-  // together.  Lane 0 of wave 0 talks to the queues; the item reaches the
-  // other waves through LDS.
+  // ---- blocks below n_static run item blockIdx.x; the others take the tail
+  // items from the queues (cca_queue.hpp)
   if ((int)blockIdx.x < P.n_static) {
     item_body(blockIdx.x);
     return;
   }
-  unsigned* const queue = g_prefill_queue + 16 * P.qslot;
+  unsigned* const slot = g_prefill_queue + 16 * P.qslot;
   __shared__ int claimed;
-  int cq = (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7u);  // XCC id
-  int dead = 0;  // queues found empty
-  const int n_tail = P.total - P.n_static;
+  int cq = tail_home_queue(), dead = 0;
   for (;;) {
-    if (tid == 0) {
-      int i = -1;
-      while (dead < 8) {
-        const unsigned s = __hip_atomic_fetch_add(queue + cq, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const long pos = cq + 8L * s;  // queue x holds tail items x, x + 8, ...
-        if (pos < n_tail) {
-          i = P.n_static + (int)pos;
-          break;
-        }
-        cq = (cq + 1) & 7;
-        ++dead;
-      }
-      claimed = i;
-    }
+    if (tid == 0) claimed = tail_claim(slot, cq, dead, P.n_static, P.total - P.n_static);
     __syncthreads();  // also: every wave is done with the previous item's LDS
     const int item = __builtin_amdgcn_readfirstlane(claimed);
     __syncthreads();  // every wave has read it before it is written again
     if (item < 0) break;
     item_body(item);
   }
-  if (tid == 0) {
-    const unsigned done = __hip_atomic_fetch_add(queue + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == gridDim.x - P.n_static - 1) {
-      for (int x = 0; x < 9; ++x) __hip_atomic_store(queue + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  if (tid == 0) tail_done(slot, gridDim.x - P.n_static);
 }
 
 constexpr int kWaves = 8;  // waves per workgroup
-
-// Compute units of the current device, looked up once per device.
-hipError_t compute_units(int* out) {
-  constexpr int kMaxDevices = 64;
-  static std::mutex mu;
-  static int counts[kMaxDevices] = {};
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (counts[dev] == 0) {
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    counts[dev] = n > 0 ? n : 1;
-  }
-  *out = counts[dev];
-  return hipSuccess;
-}
 
 int gcd_int(int a, int b) {
   while (b) {
@@ -690,7 +631,7 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
   int cus = 0;
   const hipError_t ce = compute_units(&cus);
   if (ce != hipSuccess) return ce;
-  const int n_tail = items >= 8L * cus ? (int)(items / 4) & ~7 : 0;
+  const int n_tail = tail_items(items, cus);
   P.n_static = P.total - n_tail;
   const long blocks = (long)P.n_static + std::min(n_tail, cus);
   static std::atomic<unsigned> launches{0};
