@@ -53,6 +53,14 @@
  *     storage dtype once, to nearest even.  bf16 attention feeds the matrix
  *     cores bf16 operands for raw keys and fp16 operands for cores; the
  *     probabilities are rounded to that operand type before P*V.
+ *   - Concurrency: a bf16 prefill launch (cca_attn_prefill, _ex, _chunk,
+ *     _train) that has many row blocks hands its shortest ones out through
+ *     work-queue counters held in library-owned device memory, 64 slots per
+ *     GPU taken round robin, one per launch, and cleared by the launch itself.
+ *     At most 64 such launches may be in flight on one GPU at once (across all
+ *     streams); a captured graph must not be replayed while an earlier replay
+ *     of the same graph is still running.  Calls within these limits never
+ *     share counters.
  */
 #ifndef CCA_H
 #define CCA_H

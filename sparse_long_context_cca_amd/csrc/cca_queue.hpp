@@ -4,8 +4,10 @@
 // one to a workgroup by block id, and the last n_tail (the shortest) to one
 // extra workgroup per compute unit, dispatched after all the others, that
 // takes them one at a time from eight per-XCD queues: queue x holds tail
-// items x, x + 8, x + 16, ... (n_static is a multiple of 8, so an item keeps
-// the XCD its block id would have given it).  A queue workgroup draws from its
+// items n_static + x, + 8, + 16, ...  When the item count is a multiple of 8
+// (as in the XCD-aware orders) n_static is too, so an item keeps the XCD its
+// block id would have given it; otherwise only the locality is lost.  A queue
+// workgroup draws from its
 // own XCD's queue first, then from the others in turn, so that an XCD that
 // runs faster ends up with more of the tail and the XCDs finish together.
 //
