@@ -439,6 +439,8 @@ DECODE_CASES = [
     ("bf16", 128, 2, 32, 2, 16, 64, 64, [200, 901], 20, 128),   # G = 16: the vector-ALU split kernel in bf16
     ("bf16", 64, 1, 12, 1, 4, 16, 16, [33], 25, 64),             # G = 12
     ("bf16", 128, 2, 8, 2, 100, 40, 128, [150, 399], 110, 8),    # g = 100 > w: appends at 199 and 499
+    # 512 sequences, one head each: 4096 (b, kv head) blocks of one split each
+    ("bf16", 64, 512, 8, 8, 4, 8, 8, [(37 * b) % 41 for b in range(512)], 3, 16),
 ]
 
 
@@ -555,6 +557,72 @@ def test_decode_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(outs, eager), f"replay {rep} differs"
         assert pos.tolist() == [p + steps for p in pos0]
+
+
+def test_decode_two_streams_match_sequential():
+    """Two decode loops in flight at once on two streams: both reproduce their
+    one-stream outputs bit for bit, and both positions advance once per step."""
+    say("decode on two streams")
+    B, Hq, Hkv, d, g, w, R, m_cap, steps = 3, 8, 2, 128, 4, 16, 16, 40, 40
+    pos0 = [30, 47, 64]
+    T = max(pos0) + steps
+    loops = []
+    for seed in (51, 52):
+        cfg = cfg_of("streams", B, Hq, Hkv, T, d, g, w, "bf16", seed=seed)
+        q, k, v = (x.to(DEV) for x in cca_inputs.prefill_inputs(cfg))
+        ck0 = torch.zeros((B, Hkv, m_cap, d), dtype=torch.float16, device=DEV)
+        cv0 = torch.zeros_like(ck0)
+        Lh = max(pos0)
+        ckh, cvh, _ = gpu_pool(q[:, :, :Lh].contiguous(), k[:, :, :Lh].contiguous(), v[:, :, :Lh].contiguous(), g)
+        ck0[:, :, : Lh // g] = ckh[:, :, : Lh // g]
+        cv0[:, :, : Lh // g] = cvh[:, :, : Lh // g]
+        rk0 = torch.zeros((B, Hkv, R, d), dtype=torch.bfloat16, device=DEV)
+        rv0 = torch.zeros_like(rk0)
+        for b in range(B):
+            for p in range(pos0[b] - R, pos0[b]):
+                rk0[b, :, p % R] = k[b, :, p]
+                rv0[b, :, p % R] = v[b, :, p]
+        bidx = torch.arange(B, device=DEV)
+        ts = [torch.tensor([p + i for p in pos0], device=DEV) for i in range(steps)]
+        loops.append({
+            "q": [q[bidx, :, t].contiguous() for t in ts], "k": [k[bidx, :, t].contiguous() for t in ts],
+            "v": [v[bidx, :, t].contiguous() for t in ts], "init": (ck0, cv0, rk0, rv0),
+            "ck": ck0.clone(), "cv": cv0.clone(), "rk": rk0.clone(), "rv": rv0.clone(),
+            "pos": torch.tensor(pos0, dtype=torch.int32, device=DEV),
+            "ws": torch.empty(cca.cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w), dtype=torch.uint8, device=DEV),
+            "outs": torch.empty((steps, B, Hq, d), dtype=torch.bfloat16, device=DEV)})
+
+    def reset(L):
+        for name, x0 in zip(("ck", "cv", "rk", "rv"), L["init"]):
+            L[name].copy_(x0)
+        L["pos"].copy_(torch.tensor(pos0, dtype=torch.int32, device=DEV))
+        L["outs"].zero_()
+
+    def step(L, i, stream=None):
+        cca.cca_attn_decode(L["q"][i], L["k"][i], L["v"][i], L["rk"], L["rv"], L["ck"], L["cv"], L["pos"],
+                            L["outs"][i], L["ws"], g, w, advance_pos=True, stream=stream)
+
+    for L in loops:
+        reset(L)
+        for i in range(steps):
+            step(L, i)
+    torch.cuda.synchronize()
+    ref = [L["outs"].clone() for L in loops]
+    assert all(torch.isfinite(r.float()).all() for r in ref)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        for L in loops:
+            reset(L)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            with torch.cuda.stream(s1):
+                step(loops[0], i, stream=s1)
+            with torch.cuda.stream(s2):
+                step(loops[1], i, stream=s2)
+        torch.cuda.synchronize()
+        for n, L in enumerate(loops):
+            assert torch.equal(L["outs"], ref[n]), f"stream {n + 1}, round {rep}"
+            assert L["pos"].tolist() == [p + steps for p in pos0]
 
 
 def test_decode_c5_config():
