@@ -58,9 +58,10 @@
  *     work-queue counters held in library-owned device memory, 64 slots per
  *     GPU taken round robin, one per launch, and cleared by the launch itself.
  *     At most 64 such launches may be in flight on one GPU at once (across all
- *     streams); a captured graph must not be replayed while an earlier replay
- *     of the same graph is still running.  Calls within these limits never
- *     share counters.
+ *     streams).  A launch captured into a graph keeps the slot it took at
+ *     capture for every replay, so replays that overlap in time (of one graph,
+ *     or of graphs captured with such launches) can share counters and must
+ *     not be run concurrently; sequential replays are safe.
  */
 #ifndef CCA_H
 #define CCA_H
