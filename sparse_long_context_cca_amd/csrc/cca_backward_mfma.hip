@@ -34,11 +34,13 @@
 // The pooling share of the gradients is added afterwards by the pooling
 // backward of cca_backward.hip.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "cca_device.hpp"
 #include "cca_internal.hpp"
 #include "cca_lds.hpp"
+#include "cca_queue.hpp"
 
 namespace cca {
 namespace {
@@ -398,7 +400,13 @@ struct DkvParams {
   int nCB, nSplit, nRB, UP;  // core blocks, row splits, raw blocks, units per (b, kv head)
   int xcd;
   float c, scale;
+  int total;     // units in all
+  int n_static;  // units 0 .. n_static-1 go one to a workgroup, in block order
+  int qslot;     // work-queue slot of this launch (the raw units after them)
 };
+
+// work-queue counters of the dK/dV launches in flight, one 16-word slot each
+__device__ unsigned g_dkv_queue[kQueueSlots * 16];
 
 // A workgroup of 8 waves owns 128 keys.  Waves 2p and 2p+1 share keys
 // 32p .. 32p+31 and split each 64-row tile: each computes S, dP, P and dS for
@@ -429,11 +437,14 @@ void dkv_mfma_kernel(DkvParams P) {
   const int i32 = lane & 31, hh = lane >> 5;
   const int g = P.g, w = P.w, L = P.L;
 
-  // ---- unit: core units (split-major) first, then raw-key units
-  const long bid = blockIdx.x;
-  const int BH = P.B * P.Hkv;
+  // ---- unit: core units (split-major) first, then raw-key units; the queue
+  // workgroups only ever take raw-key units (RAW_ONLY)
+  auto item = [&](const long bid, auto raw_only_tag) {
+  constexpr bool RAW_ONLY = decltype(raw_only_tag)::value;
+  const auto* const A = kernel_args<DkvParams>();
+  const int BH = A->B * A->Hkv;
   int kvp, u;
-  if (P.xcd) {
+  if (A->xcd) {
     const int hpx = BH / 8;
     const long q = bid >> 3;
     kvp = (int)(bid & 7) * hpx + (int)(q % hpx);
@@ -442,22 +453,22 @@ void dkv_mfma_kernel(DkvParams P) {
     kvp = (int)(bid % BH);
     u = (int)(bid / BH);
   }
-  const int b = kvp / P.Hkv;
+  const int b = kvp / A->Hkv;
   // core units meet fp16 cores: every product runs on fp16 operands, with Q
   // and dO from their fp16 copies; raw units run on bf16 operands
   auto unit = [&](auto core_tag) {
   constexpr bool core = decltype(core_tag)::value;
-  const uint16_t* qsrc = core ? P.q16 : P.q;
-  const uint16_t* gsrc = core ? P.do16 : P.dout;
+  const uint16_t* qsrc = core ? A->q16 : A->q;
+  const uint16_t* gsrc = core ? A->do16 : A->dout;
   int key_lo, key_lim, t_lo, t_end;
   if (core) {
-    const int split = u / P.nCB, cb = u % P.nCB;
+    const int split = u / A->nCB, cb = u % A->nCB;
     key_lo = cb * kKeysPerUnit;
-    key_lim = P.m;
+    key_lim = A->m;
     t_lo = max((key_lo + 1) * g + w - 1, split * kCoreSplit);
     t_end = min(L, (split + 1) * kCoreSplit) - 1;
   } else {
-    const int rb = u - P.nCB * P.nSplit;
+    const int rb = u - A->nCB * A->nSplit;
     key_lo = rb * kKeysPerUnit;
     key_lim = L;
     t_lo = key_lo;
@@ -467,7 +478,7 @@ void dkv_mfma_kernel(DkvParams P) {
   t_end = uni(t_end);
   if (t_lo > t_end) return;  // nothing sees these keys in this split
   const int n_rt = (t_end - t_lo) / kTileRows + 1;
-  const int n_it = P.G * n_rt;
+  const int n_it = A->G * n_rt;
 
   // ---- this pair's keys k0 .. k0+31 and this lane's key
   const int k0 = key_lo + 32 * pair;
@@ -487,8 +498,8 @@ void dkv_mfma_kernel(DkvParams P) {
   const int hi_min = core ? t_end : min(k0 + w - 1, t_end);
 
   const long kvrow = (long)kvp;
-  const uint16_t* kb_ = core ? P.ck + kvrow * P.m_cap * D : P.k + kvrow * L * D;
-  const uint16_t* vb_ = core ? P.cv + kvrow * P.m_cap * D : P.v + kvrow * L * D;
+  const uint16_t* kb_ = core ? A->ck + kvrow * A->m_cap * D : A->k + kvrow * L * D;
+  const uint16_t* vb_ = core ? A->cv + kvrow * A->m_cap * D : A->v + kvrow * L * D;
   char* vfrag = lds + 3 * SlotBytes + pair * KS * 1024 + 16 * lane;  // V fragment ks at + 1024 ks
   bf16x8 kf[KS];
 #pragma unroll
@@ -522,10 +533,10 @@ void dkv_mfma_kernel(DkvParams P) {
     const int hg = it / n_rt, tile = it % n_rt;
     const int t0 = t_lo + tile * kTileRows;
     const int nr = it < n_it ? max(0, min(kTileRows, t_end + 1 - t0)) : 0;
-    const long row = ((long)b * P.Hq + (long)(kvp % P.Hkv) * P.G + hg) * L + t0;
+    const long row = ((long)b * A->Hq + (long)(kvp % A->Hkv) * A->G + hg) * L + t0;
     const u32x4 rq = buffer_desc(qsrc + row * D, nr * D * 2);
     const u32x4 rg = buffer_desc(gsrc + row * D, nr * D * 2);
-    const u32x4 rs = buffer_desc(P.stats + row, nr * 8);
+    const u32x4 rs = buffer_desc(A->stats + row, nr * 8);
     const uint32_t qa = lds_addr(qbuf(slot)), ga = lds_addr(gbuf(slot)), sa = lds_addr(sbuf(slot));
     // load li = wave + NW i: which array it fills is uniform (a scalar select).
     // Q's last load leaves the tail (the statistics' place) alone; the
@@ -562,7 +573,7 @@ void dkv_mfma_kernel(DkvParams P) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dkt[db][r] = dvt[db][r] = 0.f;
-  const float c = P.c;
+  const float c = A->c;
 
   load_tile(0, 0);
   load_tile(1, 1);
@@ -682,26 +693,49 @@ void dkv_mfma_kernel(DkvParams P) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = 32 * db + 8 * q4 + 4 * hh;
-        *reinterpret_cast<float4*>(P.dk + orow + d0) =
-            make_float4(dkt[db][4 * q4] * P.scale, dkt[db][4 * q4 + 1] * P.scale,
-                        dkt[db][4 * q4 + 2] * P.scale, dkt[db][4 * q4 + 3] * P.scale);
-        *reinterpret_cast<float4*>(P.dv + orow + d0) =
+        *reinterpret_cast<float4*>(A->dk + orow + d0) =
+            make_float4(dkt[db][4 * q4] * A->scale, dkt[db][4 * q4 + 1] * A->scale,
+                        dkt[db][4 * q4 + 2] * A->scale, dkt[db][4 * q4 + 3] * A->scale);
+        *reinterpret_cast<float4*>(A->dv + orow + d0) =
             make_float4(dvt[db][4 * q4], dvt[db][4 * q4 + 1], dvt[db][4 * q4 + 2], dvt[db][4 * q4 + 3]);
       }
   } else {
-    const long orow = ((long)kvp * P.m + key) * D;
+    const long orow = ((long)kvp * A->m + key) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int d = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
-        atomicAdd(P.dck + orow + d, dkt[db][r] * P.scale);
-        atomicAdd(P.dcv + orow + d, dvt[db][r]);
+        atomicAdd(A->dck + orow + d, dkt[db][r] * A->scale);
+        atomicAdd(A->dcv + orow + d, dvt[db][r]);
       }
   }
   };
-  if (u < P.nCB * P.nSplit) unit(CoreTile{});
-  else unit(RawTile{});
+  if constexpr (RAW_ONLY) {
+    unit(RawTile{});
+  } else {
+    if (u < A->nCB * A->nSplit) unit(CoreTile{});
+    else unit(RawTile{});
+  }
+  };
+
+  // ---- blocks below n_static run unit blockIdx.x; the others take the tail
+  if ((int)blockIdx.x < P.n_static) {
+    item(blockIdx.x, std::false_type{});
+    return;
+  }
+  unsigned* const qslot = g_dkv_queue + 16 * P.qslot;
+  __shared__ int claimed;
+  int cq = tail_home_queue(), dead = 0;
+  for (;;) {
+    if (tid == 0) claimed = tail_claim(qslot, cq, dead, P.n_static, P.total - P.n_static);
+    __syncthreads();  // also: every wave is done with the previous unit's LDS
+    const int next = __builtin_amdgcn_readfirstlane(claimed);
+    __syncthreads();  // every wave has read it before it is written again
+    if (next < 0) break;
+    item(next, std::true_type{});
+  }
+  if (tid == 0) tail_done(qslot, gridDim.x - P.n_static);
 }
 
 constexpr int kDqWaves = 8;
@@ -788,8 +822,20 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck,
   K.c = c;
   K.scale = scale;
   const long kblocks = (long)K.UP * B * Hkv;
-  if (kblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((dkv_mfma_kernel<D>), dim3((unsigned)kblocks), dim3(512), 0, s, K);
+  if (kblocks > 0x7fffffffL / 2) return hipErrorInvalidConfiguration;
+  // the raw-key units come last in block order: the queues take the last of
+  // them (never a core unit)
+  int cus = 0;
+  const hipError_t ce = compute_units(&cus);
+  if (ce != hipSuccess) return ce;
+  const long raw_units = (long)K.nRB * B * Hkv;
+  const int n_tail = (int)std::min<long>(tail_items(kblocks, cus), raw_units & ~7L);
+  K.total = (int)kblocks;
+  K.n_static = K.total - n_tail;
+  static std::atomic<unsigned> launches{0};
+  K.qslot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
+  const long dkv_grid = (long)K.n_static + std::min(n_tail, cus);
+  hipLaunchKernelGGL((dkv_mfma_kernel<D>), dim3((unsigned)dkv_grid), dim3(512), 0, s, K);
   return hipGetLastError();
 }
 

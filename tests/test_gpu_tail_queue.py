@@ -7,6 +7,11 @@ add: slots reused across more launches than there are slots, launches on two
 streams at once, and launches replayed from a HIP graph all give the same
 outputs, bit for bit, as one eager launch (every row's arithmetic is the same
 whichever workgroup computes it), and every row is written.
+
+The backward's key-parallel kernel hands out its last raw-key units the same
+way; its gradients also take the cores' contributions through fp32 atomic
+adds, whose order varies, so there the repeated calls must agree to a few
+ulps and leave no gradient row unwritten.
 """
 from __future__ import annotations
 
@@ -117,3 +122,84 @@ def test_graph_replay_matches_eager():
         run(other)
         torch.cuda.synchronize()
         assert torch.equal(other["out"], ref_other), f"eager launch after replay {rep}"
+
+
+# ------------------------------------------------------------------ backward
+# 8 kv heads x (16 core blocks x 4 row splits + 256 raw blocks) = 2560 units
+# of the key-parallel kernel, 640 of them through the queues; a small shape
+# with no queue.
+BW_BIG = ("bw", 1, 8, 8, 32768, 128, 16, 1024)
+BW_SMALL = ("bw_small", 1, 4, 2, 700, 64, 8, 64)
+
+
+def bw_case(name, B, Hq, Hkv, L, d, g, w, seed):
+    c = case(name, B, Hq, Hkv, L, d, g, w, seed)
+    c["lse"] = torch.empty((B, Hq, L), dtype=torch.float32, device=DEV)
+    cca.cca_attn_prefill_train(c["q"], c["k"], c["v"], c["ck"], c["cv"], c["out"], c["lse"], g, w)
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    c["dout"] = torch.randn(c["q"].shape, generator=gen, device=DEV).to(c["q"].dtype)
+    c["ws"] = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g, c["q"].dtype),
+                          dtype=torch.uint8, device=DEV)
+    c["grads"] = [torch.empty((B, Hq, L, d), device=DEV), torch.empty((B, Hkv, L, d), device=DEV),
+                  torch.empty((B, Hkv, L, d), device=DEV)]
+    return c
+
+
+def bw_run(c, stream=None):
+    for t in c["grads"]:
+        t.fill_(float("nan"))
+    dq, dk, dv = c["grads"]
+    cca.cca_attn_backward(c["q"], c["k"], c["v"], c["ck"], c["cv"], c["out"], c["lse"], c["dout"],
+                          dq, dk, dv, c["ws"], c["g"], c["w"], stream=stream)
+
+
+def bw_check(c, ref, what):
+    for name, got, r in zip(("dq", "dk", "dv"), c["grads"], ref):
+        assert torch.isfinite(got).all(), f"{what}: {name} has unwritten rows"
+        tol = 1e-5 * max(1.0, float(r.abs().max()))
+        assert float((got - r).abs().max()) <= tol, f"{what}: {name} differs"
+
+
+def bw_eager(c):
+    bw_run(c)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in c["grads"]]
+    bw_check(c, ref, "eager")
+    return ref
+
+
+def test_backward_queue_slots_reused_across_calls():
+    """More backward calls than queue slots, alternating shapes with and
+    without a queue: every call writes every gradient row and agrees with the
+    first."""
+    say("backward queues: 140 calls over the queue slots")
+    big = bw_case(*BW_BIG, seed=81)
+    small = bw_case(*BW_SMALL, seed=82)
+    ref_big, ref_small = bw_eager(big), bw_eager(small)
+    for i in range(70):
+        bw_run(big)
+        if i % 10 == 9:
+            torch.cuda.synchronize()
+            bw_check(big, ref_big, f"call {i}")
+        bw_run(small)
+        if i % 10 == 9:
+            torch.cuda.synchronize()
+            bw_check(small, ref_small, f"call {i}")
+
+
+def test_backward_two_streams_at_once():
+    """Two backward calls in flight on two streams (different queue slots)."""
+    say("backward queues: two streams")
+    a = bw_case(*BW_BIG, seed=83)
+    b = bw_case(*BW_BIG, seed=84)
+    ref_a, ref_b = bw_eager(a), bw_eager(b)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(5):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            bw_run(a, stream=s1)
+        with torch.cuda.stream(s2):
+            bw_run(b, stream=s2)
+        torch.cuda.synchronize()
+        bw_check(a, ref_a, f"stream 1, round {rep}")
+        bw_check(b, ref_b, f"stream 2, round {rep}")
