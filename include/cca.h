@@ -57,9 +57,9 @@
  *     _train) that has many row blocks hands its shortest ones out through
  *     work-queue counters held in library-owned device memory, 64 slots per
  *     GPU taken round robin, one per launch, and cleared by the launch itself;
- *     so does a bf16 cca_attn_backward with many key blocks (64 slots of its
- *     own).  At most 64 launches of each kind may be in flight on one GPU at
- *     once (across all streams).  A launch captured into a graph keeps the slot it took at
+ *     so do the two main kernels of a bf16 cca_attn_backward with many row or
+ *     key blocks (64 slots each of their own).  At most 64 calls of each kind
+ *     may be in flight on one GPU at once (across all streams).  A launch captured into a graph keeps the slot it took at
  *     capture for every replay, so replays that overlap in time (of one graph,
  *     or of graphs captured with such launches) can share counters and must
  *     not be run concurrently; sequential replays are safe.

@@ -113,7 +113,13 @@ struct DqParams {
   int nPB, nHG, U;   // position blocks, head groups per kv head, units
   int xcd;
   float c, scale;
+  int total;         // items (position block x unit) in all
+  int n_static;      // items 0 .. n_static-1 go one to a workgroup, in block order
+  int qslot;         // work-queue slot of this launch (for the items after them)
 };
+
+// work-queue counters of the dQ launches in flight, one 16-word slot each
+__device__ unsigned g_dq_queue[kQueueSlots * 16];
 
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -135,25 +141,26 @@ void dq_mfma_kernel(DqParams P) {
   const int j = lane & 31, hh = lane >> 5;
 
   // ---- rows: longest first, all units of one kv head on one XCD when possible
-  const long bid = blockIdx.x;
+  auto item_body = [&](const long bid) {
+  const auto* const A = kernel_args<DqParams>();
   int pb, u;
-  if (P.xcd) {
-    const int per = P.U / 8;
+  if (A->xcd) {
+    const int per = A->U / 8;
     const long slot = bid >> 3;
     const int x = (int)(bid & 7);
-    pb = P.nPB - 1 - (int)(slot / per);
+    pb = A->nPB - 1 - (int)(slot / per);
     u = x * per + (int)(slot % per);
   } else {
-    pb = P.nPB - 1 - (int)(bid / P.U);
-    u = (int)(bid % P.U);
+    pb = A->nPB - 1 - (int)(bid / A->U);
+    u = (int)(bid % A->U);
   }
-  const int kvp = u / P.nHG, hg = u % P.nHG;
-  const int b = kvp / P.Hkv;
-  const int g = P.g, w = P.w, L = P.L;
-  const int h = (kvp % P.Hkv) * P.G + hg * P.Hw + (wave % P.Hw);
-  const int row0 = pb * P.RP + 32 * (wave / P.Hw);
-  const int P_lo = pb * P.RP;
-  const int P_hi = min(L - 1, P_lo + P.RP - 1);
+  const int kvp = u / A->nHG, hg = u % A->nHG;
+  const int b = kvp / A->Hkv;
+  const int g = A->g, w = A->w, L = A->L;
+  const int h = (kvp % A->Hkv) * A->G + hg * A->Hw + (wave % A->Hw);
+  const int row0 = pb * A->RP + 32 * (wave / A->Hw);
+  const int P_lo = pb * A->RP;
+  const int P_hi = min(L - 1, P_lo + A->RP - 1);
   const int t_raw = row0 + j;
   const int t = min(t_raw, L - 1);
   const int w_lo = uni(min(row0, L - 1)), w_hi = uni(min(row0 + 31, L - 1));
@@ -166,20 +173,20 @@ void dq_mfma_kernel(DqParams P) {
   const int n_rt = uni((P_hi - r0) / kTileRows + 1);
   const int n_tiles = uni(n_ct + n_rt);
 
-  const uint16_t* kbase = P.k + (long)kvp * L * D;
-  const uint16_t* vbase = P.v + (long)kvp * L * D;
-  const uint16_t* ckbase = P.ck + (long)kvp * P.m_cap * D;
-  const uint16_t* cvbase = P.cv + (long)kvp * P.m_cap * D;
+  const uint16_t* kbase = A->k + (long)kvp * L * D;
+  const uint16_t* vbase = A->v + (long)kvp * L * D;
+  const uint16_t* ckbase = A->ck + (long)kvp * A->m_cap * D;
+  const uint16_t* cvbase = A->cv + (long)kvp * A->m_cap * D;
 
   // ---- this lane's row: Q and dO fragments (B operands), statistics
-  const long grow = ((long)b * P.Hq + h) * L + t;
+  const long grow = ((long)b * A->Hq + h) * L + t;
   bf16x8 qf[KS], gf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = *reinterpret_cast<const bf16x8*>(P.q + grow * D + 16 * ks + 8 * hh);
-    gf[ks] = *reinterpret_cast<const bf16x8*>(P.dout + grow * D + 16 * ks + 8 * hh);
+    qf[ks] = *reinterpret_cast<const bf16x8*>(A->q + grow * D + 16 * ks + 8 * hh);
+    gf[ks] = *reinterpret_cast<const bf16x8*>(A->dout + grow * D + 16 * ks + 8 * hh);
   }
-  const float2 st = P.stats[grow];
+  const float2 st = A->stats[grow];
   const float lse2 = st.x, Dt = st.y;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(gf[ks]));
@@ -240,7 +247,7 @@ void dq_mfma_kernel(DqParams P) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqt[db][r] = 0.f;
-  const float c = P.c;
+  const float c = A->c;
   // dQ^T += K^T . dS^T for chunk cc (16 keys) and dim block db of a tile
   // (F16: a core tile)
   auto dq_mfma = [&](const char* kt, int cc, int db, const bf16x8& dsf, auto core_tag) {
@@ -266,7 +273,7 @@ void dq_mfma_kernel(DqParams P) {
   // Iteration it: K(it) in K slot it%4, V(it) in V slot it%3, K(it-1) still in
   // K slot (it-1)%4.  It loads tile it+2 (K slot (it+2)%4, V slot (it+2)%3),
   // computes S^T and dP^T of tile it, then runs the dQ product of tile it-1
-  // interleaved with tile it's P and dS (the forward's P.V / exponential
+  // interleaved with tile it's P and dS (the forward's A->V / exponential
   // interleave): chunk cc of dsb is consumed by the product just before tile
   // it's chunk cc overwrites it.  CUR and PREV say whether tiles it and it-1
   // are core tiles (fp16 operands) or raw tiles (bf16).
@@ -367,17 +374,38 @@ void dq_mfma_kernel(DqParams P) {
 
   // lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
   if (t_raw < L) {
-    float* out = P.dq + (((long)b * P.Hq + h) * L + t_raw) * D;
+    float* out = A->dq + (((long)b * A->Hq + h) * L + t_raw) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = 32 * db + 8 * q4 + 4 * hh;
         *reinterpret_cast<float4*>(out + d0) =
-            make_float4(dqt[db][4 * q4] * P.scale, dqt[db][4 * q4 + 1] * P.scale,
-                        dqt[db][4 * q4 + 2] * P.scale, dqt[db][4 * q4 + 3] * P.scale);
+            make_float4(dqt[db][4 * q4] * A->scale, dqt[db][4 * q4 + 1] * A->scale,
+                        dqt[db][4 * q4 + 2] * A->scale, dqt[db][4 * q4 + 3] * A->scale);
       }
   }
+  };
+
+  // ---- blocks below n_static run item blockIdx.x; the others take the tail
+  // from the queues.  One loop, so the item code has a single call site.
+  const bool queue_wg = (int)blockIdx.x >= P.n_static;
+  unsigned* const qs = g_dq_queue + 16 * P.qslot;
+  __shared__ int claimed;
+  int cq = tail_home_queue(), dead = 0;
+  for (;;) {
+    int item = (int)blockIdx.x;
+    if (queue_wg) {
+      if (tid == 0) claimed = tail_claim(qs, cq, dead, P.n_static, P.total - P.n_static);
+      __syncthreads();  // also: every wave is done with the previous item's LDS
+      item = __builtin_amdgcn_readfirstlane(claimed);
+      __syncthreads();  // every wave has read it before it is written again
+      if (item < 0) break;
+    }
+    item_body(item);
+    if (!queue_wg) break;
+  }
+  if (queue_wg && tid == 0) tail_done(qs, gridDim.x - P.n_static);
 }
 
 // --------------------------------------------------------------- 3. dK, dV
@@ -788,8 +816,17 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck,
   Q.c = c;
   Q.scale = scale;
   const long qblocks = (long)Q.nPB * Q.U;
-  if (qblocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3((unsigned)qblocks), dim3(64 * kDqWaves), 0, s, Q);
+  if (qblocks > 0x7fffffffL / 2) return hipErrorInvalidConfiguration;
+  int cus = 0;
+  const hipError_t ce = compute_units(&cus);
+  if (ce != hipSuccess) return ce;
+  const int q_tail = tail_items(qblocks, cus);
+  Q.total = (int)qblocks;
+  Q.n_static = Q.total - q_tail;
+  static std::atomic<unsigned> dq_launches{0};
+  Q.qslot = (int)(dq_launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
+  const long dq_grid = (long)Q.n_static + std::min(q_tail, cus);
+  hipLaunchKernelGGL((dq_mfma_kernel<D>), dim3((unsigned)dq_grid), dim3(64 * kDqWaves), 0, s, Q);
 
   DkvParams K;
   K.q = Q.q;
@@ -825,9 +862,6 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck,
   if (kblocks > 0x7fffffffL / 2) return hipErrorInvalidConfiguration;
   // the raw-key units come last in block order: the queues take the last of
   // them (never a core unit)
-  int cus = 0;
-  const hipError_t ce = compute_units(&cus);
-  if (ce != hipSuccess) return ce;
   const long raw_units = (long)K.nRB * B * Hkv;
   const int n_tail = (int)std::min<long>(tail_items(kblocks, cus), raw_units & ~7L);
   K.total = (int)kblocks;

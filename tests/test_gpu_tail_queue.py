@@ -8,8 +8,9 @@ streams at once, and launches replayed from a HIP graph all give the same
 outputs, bit for bit, as one eager launch (every row's arithmetic is the same
 whichever workgroup computes it), and every row is written.
 
-The backward's key-parallel kernel hands out its last raw-key units the same
-way; its gradients also take the cores' contributions through fp32 atomic
+The backward's kernels hand out their last items the same way (the dQ kernel
+its shortest position blocks, the key-parallel kernel its last raw-key
+units); the gradients also take the cores' contributions through fp32 atomic
 adds, whose order varies, so there the repeated calls must agree to a few
 ulps and leave no gradient row unwritten.
 """
@@ -125,10 +126,11 @@ def test_graph_replay_matches_eager():
 
 
 # ------------------------------------------------------------------ backward
-# 8 kv heads x (16 core blocks x 4 row splits + 256 raw blocks) = 2560 units
-# of the key-parallel kernel, 640 of them through the queues; a small shape
-# with no queue.
-BW_BIG = ("bw", 1, 8, 8, 32768, 128, 16, 1024)
+# The key-parallel kernel: 8 kv heads x (32 core blocks x 8 row splits + 512
+# raw blocks) = 6144 units, 1536 of them through the queues; the row-parallel
+# dQ kernel: 256 position blocks x 8 heads = 2048 items, 512 through its
+# queues.  A small shape with no queue.
+BW_BIG = ("bw", 1, 8, 8, 65536, 128, 16, 1024)
 BW_SMALL = ("bw_small", 1, 4, 2, 700, 64, 8, 64)
 
 
