@@ -91,8 +91,12 @@ __device__ __forceinline__ float pair_max(float x) {
 }
 
 // Two waves per SIMD (the accumulators stay in arch VGPRs, 256 per wave) so
-// that one wave's softmax overlaps the other's matrix ops.
-template <int D, int OT, int NW>
+// that one wave's softmax overlaps the other's matrix ops.  OFF > 0 (a
+// workgroup of one head's 256 consecutive rows): the second half of the waves
+// walks the raw window up to OFF tiles ahead of the first half, so that each
+// half steps only through the window it needs (about 18 tiles at w = 1024)
+// instead of the union of all rows' windows (20).
+template <int D, int OT, int NW, int OFF>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillParams P) {
   constexpr int kThreads = 64 * NW;
@@ -109,8 +113,15 @@ void prefill_mfma_kernel(PrefillParams P) {
   constexpr int NVI = VBytes / 1024;    // 1 KB wave loads per V tile
   static_assert(NVI % NW == 0, "V wave loads split evenly over the waves");
   constexpr int NVW = NVI / NW;
-  // LDS: a ring of three K tiles and a ring of three V tiles
-  __shared__ __attribute__((aligned(16))) char lds[3 * KBytes + 3 * VBytes];
+  // LDS: rings of K and V tiles, K(q) in slot q % NSK and V(q) in q % NSV
+  // for tile q of the walk.  OFF = 0: three K slots (K loaded two tiles
+  // ahead) and three V slots (V one tile ahead of its scores).  OFF > 0: the
+  // leading half may be OFF tiles ahead, so OFF + 3 K slots, and OFF + 2 V
+  // slots with V loaded in the stage that computes the leading half's scores
+  // of its tile.
+  constexpr int NSK = OFF + 3;
+  constexpr int NSV = OFF == 0 ? 3 : OFF + 2;
+  __shared__ __attribute__((aligned(16))) char lds[NSK * KBytes + NSV * VBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -185,6 +196,21 @@ void prefill_mfma_kernel(PrefillParams P) {
   const int r0 = raw_lo & ~(kBK - 1);
   const int n_rt = uni((P_hi - r0) / kBK + 1);
   const int n_tiles = uni(n_ct + n_rt);
+  // ---- the halves (OFF > 0): waves 0 .. NW/2-1 hold rows P_lo .. mid-1 and
+  // need raw tiles 0 .. a_last; the leading half (the other waves) needs raw
+  // tiles from b_first on and walks them off_b tiles ahead, so the raw walk
+  // takes n_rt - off_b steps (off_b <= b_first keeps every tile the leading
+  // half needs in its walk, off_b <= n_rt-1-a_last every tile of the other).
+  // Both halves then walk the same core tiles, tile s + off_b at step s.
+  int off_b = 0;
+  if constexpr (OFF > 0) {
+    const int mid = P_lo + A->RP / 2;
+    const int a_last = (min(mid - 1, Le - 1) - r0) / kBK;
+    const int b_first = (win_lo(min(mid, Le - 1), w) - r0) / kBK;
+    off_b = uni(max(0, min(min(OFF, b_first), n_rt - 1 - a_last)));
+  }
+  const int lead_off = (OFF > 0 && wave >= NW / 2) ? off_b : 0;
+  const int n_raw_steps = n_rt - off_b;
 
   const long kvrow = (long)kvp;
   const uint16_t* kbase = A->k + kvrow * A->Lk * D;
@@ -240,9 +266,9 @@ void prefill_mfma_kernel(PrefillParams P) {
     const uint16_t* src = (core ? (values ? cvbase : ckbase) : (values ? vbase : kbase)) + (long)base * D;
     return buffer_desc(src, nbytes);
   };
-  // LDS: [K ring 0 | K ring 1 | K ring 2 | V ring 0 | V ring 1 | V ring 2]
+  // LDS: [K ring slots 0 .. NSK-1 | V ring slots 0 .. NSV-1]
   auto kbuf = [&](int i) { return lds + i * KBytes; };
-  auto vbuf = [&](int i) { return lds + 3 * KBytes + i * VBytes; };
+  auto vbuf = [&](int i) { return lds + NSK * KBytes + i * VBytes; };
   auto load_k = [&](int slot, int it) {  // K(it) -> K ring slot (wave-uniform)
     const u32x4 r = rsrc(it, false);
     const uint32_t base = lds_addr(kbuf(slot));
@@ -320,20 +346,31 @@ void prefill_mfma_kernel(PrefillParams P) {
   // End of a pipeline stage: this wave's loads of the previous stage (K(it+1),
   // V(it)) have landed in LDS, then the workgroup meets.  Loads finish in
   // issue order, so allowing this stage's loads (K(it+2): at least NKMIN wave
-  // loads; V(it+1): NVW) to stay in flight is enough.
-  constexpr int kInFlight = NKMIN + NVW;
+  // loads; V(it+1): NVW) to stay in flight is enough.  OFF > 0: a stage
+  // issues its V tile before its K tile, and the V tile must land in it.
+  constexpr int kInFlight = OFF == 0 ? NKMIN + NVW : NKMIN;
   auto sync_stage = [&]() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kInFlight) : "memory");
   };
 
   // prologue: K(0), K(1) into K slots 0, 1 and V(0) into V slot 0; V slot 2
   // (read as "tile -1", with zero probabilities) cleared so it holds no NaN
-  load_k(0, 0);
-  load_k(1, 1);
-  load_v(0, 0);
+  // OFF > 0: K(0 .. off_b) and V(0 .. off_b-1) land before the walk and
+  // K(off_b+1) in its first stage; V slot NSV-1 is tile -1's.
+  if constexpr (OFF == 0) {
+    load_k(0, 0);
+    load_k(1, 1);
+    load_v(0, 0);
+  } else {
+#pragma unroll 1
+    for (int x = 0; x <= off_b; ++x) load_k(x, x);
+#pragma unroll 1
+    for (int x = 0; x < off_b; ++x) load_v(x, x);
+    load_k(off_b + 1, off_b + 1);
+  }
   for (int i = tid; i < VBytes / 16; i += kThreads)
-    *reinterpret_cast<u32x4*>(vbuf(2) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NKMIN + NVW) : "memory");
+    *reinterpret_cast<u32x4*>(vbuf(NSV - 1) + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(OFF == 0 ? NKMIN + NVW : NKMIN) : "memory");
   // probabilities of the previous tile, the B operands of its P.V: bf16 for
   // a raw tile (pr), fp16 for a core tile (prh); each walk starts them at zero
   bf16x8 pr[4];
@@ -353,12 +390,26 @@ void prefill_mfma_kernel(PrefillParams P) {
   // and the exponentials share one scheduling region.
   bool grow_pending = false;
   float alpha_pending = 1.0f;
-  int kslot = 0;  // it % 3
-  auto iteration = [&](int it, auto cur_tag, auto prev_tag) {
+  int kslot = 0;  // it % 3 (OFF = 0)
+  // Step st, this wave's tile it (it = st unless the wave's half is ahead).
+  auto iteration = [&](int st, int it, auto cur_tag, auto prev_tag) {
     constexpr bool CUR = decltype(cur_tag)::value, PREV = decltype(prev_tag)::value;
-    const int prev = kslot == 0 ? 2 : kslot - 1, next = kslot == 2 ? 0 : kslot + 1;
-    load_k(prev, it + 2);  // empty (zeros) past the last tile
-    load_v(next, it + 1);
+    int k_cur, v_prev, k_next = 0;  // K slot of tile it, V slot of tile it-1
+    if constexpr (OFF == 0) {
+      (void)st;
+      const int prev = kslot == 0 ? 2 : kslot - 1, next = kslot == 2 ? 0 : kslot + 1;
+      load_k(prev, it + 2);  // empty (zeros) past the last tile
+      load_v(next, it + 1);
+      k_cur = kslot;
+      v_prev = prev;
+      k_next = next;
+    } else {
+      const int ql = st + off_b;  // the leading half's tile
+      load_v(ql % NSV, ql);
+      load_k((ql + 2) % NSK, ql + 2);
+      k_cur = it % NSK;
+      v_prev = (it + NSV - 1) % NSV;
+    }
     if (grow_pending) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -366,8 +417,8 @@ void prefill_mfma_kernel(PrefillParams P) {
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha_pending;
       rescale_sums(alpha_pending);
     }
-    const char* kt = kbuf(kslot);
-    const char* vt_prev = vbuf(prev);
+    const char* kt = kbuf(k_cur);
+    const char* vt_prev = vbuf(v_prev);
     f32x16 sx[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -466,7 +517,7 @@ void prefill_mfma_kernel(PrefillParams P) {
     }
     grow_pending = __builtin_amdgcn_ballot_w64(grow) != 0;
     alpha_pending = alpha;
-    kslot = next;
+    if constexpr (OFF == 0) kslot = k_next;
     sync_stage();
   };
   // the rescale the last tile's new max asked for, before a P.V that runs
@@ -481,12 +532,18 @@ void prefill_mfma_kernel(PrefillParams P) {
     }
     grow_pending = false;
   };
-  // The P.V of a walk's last tile, outside the pipeline: V(last) sits in the
-  // V slot before the next load slot.
-  auto flush_tile = [&](auto core_tag) {
+  // The P.V of a walk's last tile (this wave's tile last), outside the
+  // pipeline.  OFF = 0: V(last) sits in the V slot before the next load slot.
+  auto flush_tile = [&](int last, auto core_tag) {
     constexpr bool CORE = decltype(core_tag)::value;
     apply_pending_rescale();
-    const char* vt = vbuf(kslot == 0 ? 2 : kslot - 1);
+    const char* vt;
+    if constexpr (OFF == 0) {
+      (void)last;
+      vt = vbuf(kslot == 0 ? 2 : kslot - 1);
+    } else {
+      vt = vbuf(last % NSV);
+    }
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
@@ -511,9 +568,9 @@ void prefill_mfma_kernel(PrefillParams P) {
   for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
     for (int e = 0; e < 8; ++e) pr[cc][e] = static_cast<__bf16>(0.0f);
-  for (int it = 0; it < n_rt; ++it) iteration(it, RawTile{}, RawTile{});
+  for (int st = 0; st < n_raw_steps; ++st) iteration(st, st + lead_off, RawTile{}, RawTile{});
   if (n_ct > 0) {
-    flush_tile(RawTile{});
+    flush_tile(n_raw_steps - 1 + lead_off, RawTile{});
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16_frag_to_f16(qf[ks]);
     sel = selector(CoreTile{});
@@ -521,13 +578,13 @@ void prefill_mfma_kernel(PrefillParams P) {
     for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) prh[cc][e] = static_cast<_Float16>(0.0f);
-    for (int it = n_rt; it < n_tiles; ++it) iteration(it, CoreTile{}, CoreTile{});
+    for (int st = n_raw_steps; st < n_tiles - off_b; ++st) iteration(st, st + off_b, CoreTile{}, CoreTile{});
   }
   // the loads issued for tiles past the end must land before the workgroup's
   // LDS can be handed to another
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (n_ct > 0) flush_tile(CoreTile{});  // the walk's last tile
-  else flush_tile(RawTile{});
+  if (n_ct > 0) flush_tile(n_tiles - 1, CoreTile{});  // the walk's last tile
+  else flush_tile(n_raw_steps - 1 + lead_off, RawTile{});
 
   // ---- normalise and store: lane holds dims 32db + 8(r/4) + 4hh + r%4 of row j
   // row j's sum: lane j%16 holds it, in lsum[0] for j < 16 and lsum[1] above
@@ -636,12 +693,26 @@ hipError_t launch_prefill_mfma(const void* q, const void* k, const void* v, cons
   const long blocks = (long)P.n_static + std::min(n_tail, cus);
   static std::atomic<unsigned> launches{0};
   P.qslot = (int)(launches.fetch_add(1, std::memory_order_relaxed) % kQueueSlots);
+  // one head per workgroup (256 consecutive rows): the halves walk the raw
+  // window apart
+  const dim3 grid((unsigned)blocks), block(64 * kWaves);
+  const bool halves = P.Hw == 1;
   if (sh.d == 64) {
-    if (out_dt == 1) hipLaunchKernelGGL((prefill_mfma_kernel<64, 1, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<64, 0, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
+    if (out_dt == 1) {
+      if (halves) hipLaunchKernelGGL((prefill_mfma_kernel<64, 1, kWaves, 2>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((prefill_mfma_kernel<64, 1, kWaves, 0>), grid, block, 0, s, P);
+    } else {
+      if (halves) hipLaunchKernelGGL((prefill_mfma_kernel<64, 0, kWaves, 2>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((prefill_mfma_kernel<64, 0, kWaves, 0>), grid, block, 0, s, P);
+    }
   } else {
-    if (out_dt == 1) hipLaunchKernelGGL((prefill_mfma_kernel<128, 1, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<128, 0, kWaves>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, P);
+    if (out_dt == 1) {
+      if (halves) hipLaunchKernelGGL((prefill_mfma_kernel<128, 1, kWaves, 2>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((prefill_mfma_kernel<128, 1, kWaves, 0>), grid, block, 0, s, P);
+    } else {
+      if (halves) hipLaunchKernelGGL((prefill_mfma_kernel<128, 0, kWaves, 2>), grid, block, 0, s, P);
+      else hipLaunchKernelGGL((prefill_mfma_kernel<128, 0, kWaves, 0>), grid, block, 0, s, P);
+    }
   }
   return hipGetLastError();
 }
