@@ -480,7 +480,7 @@ def main():
                    "seq_len": cfg.L, "head_dim": cfg.d, "group": cfg.g, "window": cfg.w},
         "roofline": {
             "bound": "mfma",
-            "kernel": "prefill_mfma_kernel<128,1,8>",
+            "kernel": "prefill_mfma_kernel<128,1,8,0>",
             "achieved": tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
