@@ -102,13 +102,16 @@ def test_chunked_prefill_equals_full_prefill(case):
     assert torch.isnan(ck[:, :, m:]).all(), "no core beyond the completed groups"
 
 
-def test_variable_length_batch():
+@pytest.mark.parametrize("heads,w", [((8, 2), 64), ((4, 4), 300)], ids=["G4-w64", "G1-w300"])
+def test_variable_length_batch(heads, w):
     """One call per step for a batch whose sequences sit at their own offsets
     and lengths (one of them empty in the first step); output rows past each
-    sequence's length stay untouched."""
-    dt, B, Hq, Hkv, d, g, w = "bf16", 3, 8, 2, 128, 16, 64
+    sequence's length stay untouched.  With one query head per kv head the
+    workgroups' halves walk the raw window apart, from offsets that start
+    mid-tile."""
+    (Hq, Hkv), dt, B, d, g = heads, "bf16", 3, 128, 16
     L = 600
-    say("variable-length batch")
+    say(f"variable-length batch Hq={Hq} Hkv={Hkv} w={w}")
     q, k, v = inputs(dt, B, Hq, Hkv, L, d, g, w, seed=811)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     m_cap = L // g

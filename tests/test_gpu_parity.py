@@ -188,6 +188,7 @@ PREFILL_CASES = [
     (2, 32, 16, 600, 128, 16, 128),   # 32 (batch, kv head) units: four per XCD across the batch
     (1, 8, 2, 6000, 64, 16, 256),     # d = 64, G = 4: eight core tiles, a ragged last block
     (2, 4, 4, 3500, 64, 8, 100),      # d = 64, one query head per kv head, g = 8
+    (1, 2, 2, 2600, 128, 16, 700),    # one head per workgroup, a window of 11 tiles less 4 keys
 ]
 
 
