@@ -273,7 +273,7 @@ void dq_mfma_kernel(DqParams P) {
   // Iteration it: K(it) in K slot it%4, V(it) in V slot it%3, K(it-1) still in
   // K slot (it-1)%4.  It loads tile it+2 (K slot (it+2)%4, V slot (it+2)%3),
   // computes S^T and dP^T of tile it, then runs the dQ product of tile it-1
-  // interleaved with tile it's P and dS (the forward's A->V / exponential
+  // interleaved with tile it's P and dS (the forward's P.V / exponential
   // interleave): chunk cc of dsb is consumed by the product just before tile
   // it's chunk cc overwrites it.  CUR and PREV say whether tiles it and it-1
   // are core tiles (fp16 operands) or raw tiles (bf16).
