@@ -12,15 +12,13 @@
 //   dq_t = sum_k dS key_k / sqrt(d)                      (dq_mfma_kernel)
 //   dkey_k = sum_t dS q_t / sqrt(d), dvalue_k = sum_t P dO_t   (dkv_mfma_kernel)
 // Kernels, in launch order:
-//   1. row_stats_kernel  per row {lse * log2(e), D_t}, and fp16 copies of q
-//                        and dO for the core products
-//   2. dq_mfma_kernel    row-parallel, the forward's work decomposition: per
+//   1. dq_mfma_kernel    row-parallel, the forward's work decomposition: per
 //                        64-key tile S^T = K.Q^T and dP^T = V.dO^T (K, V rows
 //                        from LDS, Q and dO fragments in registers), and
 //                        dQ^T += K^T.dS^T with K^T through transposing reads;
 //                        the dQ product of tile i-1 is interleaved with tile
 //                        i's exponentials, as in the forward
-//   3. dkv_mfma_kernel   key-parallel: a workgroup owns 128 keys (raw
+//   2. dkv_mfma_kernel   key-parallel: a workgroup owns 128 keys (raw
 //                        positions, or cores) of one kv head and walks the
 //                        rows that see them for every query head of the
 //                        group.  A pair of waves shares 32 keys (K fragments
@@ -51,53 +49,10 @@ constexpr int kTileRows = 64;    // keys per tile (dQ), rows per tile (dK dV)
 constexpr int kKeysPerUnit = 128;  // keys per dK dV workgroup (4 wave pairs x 32)
 constexpr int kCoreSplit = 8192;   // rows per core unit (absolute, aligned splits)
 
-// ------------------------------------------------------------- 1. statistics
-
-// stats[row] = {lse[row] * log2(e), dO_row . O_row}; 16 lanes per row.  The
-// pass also writes fp16 copies of the row's q and dO (q16, do16): the core
-// products of the dK/dV kernel take their Q and dO tiles from them, since the
-// cores they meet are fp16.
-template <int D>
-__global__ __launch_bounds__(256) void row_stats_kernel(const uint16_t* __restrict__ out,
-                                                        const uint16_t* __restrict__ dout,
-                                                        const uint16_t* __restrict__ q,
-                                                        const float* __restrict__ lse,
-                                                        float2* __restrict__ stats,
-                                                        uint16_t* __restrict__ q16,
-                                                        uint16_t* __restrict__ do16, long rows) {
-  constexpr int LPR = 16, EPL = D / LPR, NW = EPL / 2;  // NW dwords (bf16 pairs) per lane
-  typedef uint32_t words __attribute__((ext_vector_type(NW)));
-  const long row = ((long)blockIdx.x * blockDim.x + threadIdx.x) / LPR;
-  const int part = threadIdx.x % LPR;
-  const bool valid = row < rows;
-  float acc = 0.f;
-  if (valid) {
-    const long off = row * D + part * EPL;
-    const words o = *reinterpret_cast<const words*>(out + off);
-    const words gg = *reinterpret_cast<const words*>(dout + off);
-    const words qq = *reinterpret_cast<const words*>(q + off);
-    words q16w, g16w;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const float o0 = __uint_as_float(o[i] << 16), o1 = __uint_as_float(o[i] & 0xffff0000u);
-      const float g0 = __uint_as_float(gg[i] << 16), g1 = __uint_as_float(gg[i] & 0xffff0000u);
-      acc = fmaf(o0, g0, acc);
-      acc = fmaf(o1, g1, acc);
-      g16w[i] = pack_f16x2(g0, g1);
-      q16w[i] = pack_f16x2(__uint_as_float(qq[i] << 16), __uint_as_float(qq[i] & 0xffff0000u));
-    }
-    *reinterpret_cast<words*>(q16 + off) = q16w;
-    *reinterpret_cast<words*>(do16 + off) = g16w;
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (valid && part == 0) stats[row] = make_float2(lse[row] * kLog2e, acc);
-}
-
 // A wave-uniform value held in a scalar register.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// ------------------------------------------------------------------ 2. dQ
+// ------------------------------------------------------------------ 1. dQ
 
 struct DqParams {
   const uint16_t* q;
@@ -106,7 +61,11 @@ struct DqParams {
   const uint16_t* ck;
   const uint16_t* cv;
   const uint16_t* dout;
-  const float2* stats;
+  const uint16_t* out;
+  const float* lse;
+  float2* stats;     // written here: per row {lse * log2(e), dO . O}
+  uint16_t* q16;     // written here: fp16 copies of q and dout, for the dK dV kernel
+  uint16_t* do16;
   float* dq;
   int B, Hq, Hkv, L, g, w, m_cap;
   int G, Hw, RP;     // heads per workgroup, rows per head per workgroup
@@ -180,14 +139,32 @@ void dq_mfma_kernel(DqParams P) {
 
   // ---- this lane's row: Q and dO fragments (B operands), statistics
   const long grow = ((long)b * A->Hq + h) * L + t;
+  // The row's statistics are made here: D_t = dO_t . o_t (the lane's half
+  // of the dims, plus its partner lane's), lse in base 2.  The lane that owns
+  // row t (lanes past the sequence end repeat row L-1) also stores them, with
+  // fp16 copies of its q and dO fragments, for the dK dV kernel.
   bf16x8 qf[KS], gf[KS];
+  float dacc = 0.f;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qf[ks] = *reinterpret_cast<const bf16x8*>(A->q + grow * D + 16 * ks + 8 * hh);
-    gf[ks] = *reinterpret_cast<const bf16x8*>(A->dout + grow * D + 16 * ks + 8 * hh);
+    const long e0 = grow * D + 16 * ks + 8 * hh;
+    qf[ks] = *reinterpret_cast<const bf16x8*>(A->q + e0);
+    gf[ks] = *reinterpret_cast<const bf16x8*>(A->dout + e0);
+    const bf16x8 of = *reinterpret_cast<const bf16x8*>(A->out + e0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dacc = fmaf(static_cast<float>(of[e]), static_cast<float>(gf[ks][e]), dacc);
   }
-  const float2 st = A->stats[grow];
-  const float lse2 = st.x, Dt = st.y;
+  const float Dt = dacc + __shfl_xor(dacc, 32, 64);
+  const float lse2 = A->lse[grow] * kLog2e;
+  if (t_raw < L) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const long e0 = grow * D + 16 * ks + 8 * hh;
+      *reinterpret_cast<bf16x8*>(A->q16 + e0) = bf16_frag_to_f16(qf[ks]);
+      *reinterpret_cast<bf16x8*>(A->do16 + e0) = bf16_frag_to_f16(gf[ks]);
+    }
+    if (hh == 0) A->stats[grow] = make_float2(lse2, Dt);
+  }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]), "v"(gf[ks]));
   asm volatile("" ::"v"(lse2), "v"(Dt));
@@ -353,6 +330,9 @@ void dq_mfma_kernel(DqParams P) {
   if (n_ct > 0) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      // converted again rather than kept from the prologue's stores, which
+      // would hold 16 more fragments live through the raw tiles
+      asm volatile("" : "+v"(qf[ks]), "+v"(gf[ks]));
       qf[ks] = bf16_frag_to_f16(qf[ks]);
       gf[ks] = bf16_frag_to_f16(gf[ks]);
     }
@@ -408,7 +388,7 @@ void dq_mfma_kernel(DqParams P) {
   if (queue_wg && tid == 0) tail_done(qs, gridDim.x - P.n_static);
 }
 
-// --------------------------------------------------------------- 3. dK, dV
+// --------------------------------------------------------------- 2. dK, dV
 
 struct DkvParams {
   const uint16_t* q;
@@ -417,7 +397,7 @@ struct DkvParams {
   const uint16_t* ck;
   const uint16_t* cv;
   const uint16_t* dout;
-  const uint16_t* q16;   // fp16 copies of q and dout (row_stats_kernel), read by core units
+  const uint16_t* q16;   // fp16 copies of q and dout (written by the dQ kernel), read by core units
   const uint16_t* do16;
   const float2* stats;
   float* dk;   // raw-key gradients [B,Hkv,L,d]
@@ -785,10 +765,6 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck,
   const int B = sh.B, Hq = sh.Hq, Hkv = sh.Hkv, L = sh.L, g = sh.g, w = sh.w;
   const int m = L / g;
   const float scale = 1.0f / sqrtf((float)D), c = kLog2e * scale;
-  const long rows = (long)B * Hq * L;
-  hipLaunchKernelGGL((row_stats_kernel<D>), dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout),
-                     static_cast<const uint16_t*>(q), lse, stats, q16, do16, rows);
 
   DqParams Q;
   Q.q = static_cast<const uint16_t*>(q);
@@ -797,7 +773,11 @@ hipError_t launch_t(const void* q, const void* k, const void* v, const void* ck,
   Q.ck = static_cast<const uint16_t*>(ck);
   Q.cv = static_cast<const uint16_t*>(cv);
   Q.dout = static_cast<const uint16_t*>(dout);
+  Q.out = static_cast<const uint16_t*>(out);
+  Q.lse = lse;
   Q.stats = stats;
+  Q.q16 = q16;
+  Q.do16 = do16;
   Q.dq = dq;
   Q.B = B;
   Q.Hq = Hq;
