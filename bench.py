@@ -11,7 +11,9 @@ under "backward": the backward pass over the headline workload; under
 "decode": the decode workload (batch 8, 32/8 heads, 65536 cached tokens, 256
 single-token steps).  A large bf16 GEMM, a device-to-device copy and a
 read-only reduction give measured ceilings ("reference_rates") next to the
-spec peaks.
+spec peaks, and so does a kernel that runs nothing but matrix-core work on
+random operands (libcca_probe.so): the rate the matrix cores sustain on this
+chip, at the clock its power limit allows.
 
 Prints ONE JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
 --warmup W, --no-cpu (skip the CPU-oracle baseline), --no-decode, --no-backward,
@@ -79,10 +81,18 @@ def measured_mfma_busy(name, kernel="mfma_busy_fraction"):
 
 def code_digest(sources):
     """SHA-256 over the code lines of the given sources (// comments and blank
-    lines dropped, so that editing a comment keeps a counter figure valid)."""
+    lines dropped, so that editing a comment keeps a counter figure valid).  Of
+    the build script only its compiler-flag block counts (the lines between
+    its "---- compiler flags" and "---- end of compiler flags" markers): the
+    rest of the script does not change what a kernel executes."""
     h = hashlib.sha256()
     for src in sources:
-        for line in open(os.path.join(ROOT, src), encoding="utf-8"):
+        lines = open(os.path.join(ROOT, src), encoding="utf-8").read().splitlines(True)
+        if src.endswith("build.py"):
+            start = next(i for i, ln in enumerate(lines) if "---- compiler flags" in ln)
+            end = next(i for i, ln in enumerate(lines) if "---- end of compiler flags" in ln)
+            lines = lines[start:end + 1]
+        for line in lines:
             code = line.split("//", 1)[0].rstrip()
             if code:
                 h.update(code.encode() + b"\n")
@@ -350,6 +360,38 @@ def reference_rates(dev="cuda:0", n=16384, copy_bytes=1 << 30, read_rows=65536, 
                          "bytes read per pass"}
 
 
+def mfma_ceiling(dev="cuda:0", iters=50000, reps=3, operand_sets=4):
+    """The rate the matrix cores sustain on this chip doing nothing else:
+    libcca_probe.so's kernel (one 8-wave workgroup per compute unit, back-to-back
+    32x32x16 bf16 MFMAs on random register operands that rotate over four sets),
+    timed with events on torch's stream after one short warm-up launch.  The
+    operands are random because the chip's power, and with it the clock, depends
+    on the bits the multipliers see: constant operands run much faster than any
+    real kernel can."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_long_context_cca_amd", "libcca_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.cca_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint,
+                                   ctypes.c_void_p]
+    blocks = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    assert lib.cca_probe_mfma(out.data_ptr(), blocks, iters // 10, operand_sets, 1, stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        assert lib.cca_probe_mfma(out.data_ptr(), blocks, iters, operand_sets, 2 + r, stream) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = blocks * 8.0 * iters * 16 * 32768
+    return {"mfma_random_TFLOP_per_s": flops / (ms * 1e-3) / 1e12, "mfma_probe_ms": ms,
+            "mfma_note": f"{blocks} workgroups x 8 waves, back-to-back v_mfma_f32_32x32x16_bf16 on random "
+                         f"register operands rotating over {operand_sets} sets (libcca_probe.so)"}
+
+
 def bench_decode(cca, cfg, steps_timed=True):
     """256 sequential decode steps over a 65536-token cache; one timed region."""
     B, Hq, Hkv, d, g, w, L, S = cfg.B, cfg.Hq, cfg.Hkv, cfg.d, cfg.g, cfg.w, cfg.L, cfg.decode_steps
@@ -535,8 +577,13 @@ def main():
     # decode against a device-to-device copy
     print("[bench] reference rates", file=sys.stderr, flush=True)
     ref = reference_rates()
+    ceiling = mfma_ceiling()
+    if ceiling is not None:
+        ref.update(ceiling)
     result["reference_rates"] = ref
     result["roofline"]["frac_of_measured_gemm"] = tflops / ref["bf16_gemm_TFLOP_per_s"]
+    if ceiling is not None:
+        result["roofline"]["frac_of_mfma_ceiling"] = tflops / ceiling["mfma_random_TFLOP_per_s"]
     if result["pool"]["GB_per_s"]:
         result["pool"]["frac_of_measured_copy"] = result["pool"]["GB_per_s"] / ref["d2d_copy_GB_per_s"]
     if "decode" in result:

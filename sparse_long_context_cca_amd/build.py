@@ -19,7 +19,13 @@ LIB = os.path.join(PKG, "libcca.so")
 SOURCES = ["cca_api.hip", "cca_pool.hip", "cca_prefill_valu.hip", "cca_prefill_mfma.hip",
            "cca_decode.hip", "cca_backward.hip", "cca_backward_mfma.hip"]
 
+# the matrix-core probe that bench.py times beside the kernels (a library of its own)
+PROBE_SOURCES = ["cca_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libcca_probe.so")
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# ---- compiler flags (the lines up to the end marker are what a counter
+# summary's digest covers of this script; see bench.py's code_digest)
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled: only scalar fp32 arithmetic is emitted.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -32,6 +38,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.
 SOURCE_FLAGS = {
     "cca_prefill_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
 }
+# ---- end of compiler flags
 
 
 def _compile(src: str) -> str:
@@ -85,8 +92,9 @@ def build_sanitized(objs=None) -> str:
 
 
 def build(verbose: bool = True) -> str:
-    """Compiles every source for gfx950 and links libcca.so (and the
-    host-sanitized libcca_asan.so for the CPU tests); returns libcca.so's path."""
+    """Compiles every source for gfx950 and links libcca.so, the matrix-core
+    probe libcca_probe.so and the host-sanitized libcca_asan.so for the CPU
+    tests; returns libcca.so's path."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(OBJ, exist_ok=True)
@@ -99,6 +107,13 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     shutil.move(tmp, LIB)
+    probe_objs = [_compile(s) for s in PROBE_SOURCES]
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *probe_objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    shutil.move(tmp, PROBE_LIB)
     build_sanitized(objs)
     if verbose:
         print(f"built {LIB} from {len(objs)} sources (and {SAN_LIB})", file=sys.stderr)

@@ -83,3 +83,21 @@ def test_a_changed_kernel_drops_the_figures(tmp_path):
 def test_a_missing_summary_gives_no_figure(tmp_path):
     (tmp_path / "profiles").mkdir()
     assert _with_root(tmp_path, lambda: bench.measured_traffic("absent")) is None
+
+
+def _build_script(flags_line, other_line):
+    return ("import os\n" + other_line + "\n# ---- compiler flags (covered)\nARCH = 'gfx950'\n" + flags_line +
+            "\n# ---- end of compiler flags\n\ndef build():\n    pass\n")
+
+
+def test_build_script_digest_covers_its_flag_block_only(tmp_path):
+    """Of a build script only the compiler-flag block enters the digest: a
+    change elsewhere in it (a new library to link, say) keeps the counter
+    figures, a changed flag drops them."""
+    def digest(text):
+        (tmp_path / "build.py").write_text(text)
+        return _with_root(tmp_path, lambda: bench.code_digest(["build.py"]))
+    base = digest(_build_script("COMMON = ['-O3']", "X = 1"))
+    assert digest(_build_script("COMMON = ['-O3']", "X = 2  # another library")) == base
+    assert digest(_build_script("COMMON = ['-O2']", "X = 1")) != base
+
