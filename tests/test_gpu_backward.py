@@ -5,8 +5,9 @@ Both sides take the same seeded input bits and the same upstream gradient.
 The GPU's backward runs on the cores and the output its forward produced
 (rounded to the storage dtype), the oracle on its own exact forward, so the
 bar is relative to the gradient's scale: max |err| <= tol * max(1, max |ref|).
-The bars sit about 1.5x above what the kernels achieve over these cases and
-the full-size one: tol 6e-3 for bf16 inputs (largest seen 4.1e-3: P and dS
+The bars sit above what the kernels achieve over these cases and the
+full-size ones: tol 6e-3 for bf16 inputs (largest seen 5.3e-3, dq of one kv
+head of the 32K MHA workload, whose scale is 1.1; 4.2e-3 elsewhere: P and dS
 rounded to the operand type before their products, the bf16 output, the
 fp16 cores) and 2e-6 for fp32 inputs (largest seen 3.0e-7); the row
 log-sum-exp within 5e-3 (bf16; largest seen 1.8e-3) and 1e-5 (fp32; 7.5e-7).
@@ -94,6 +95,8 @@ BWD_CASES = [
     ("bf16", 1, 4, 2, 40, 128, 64, 8, cca.CCA_POOL_MAX),         # g > L: no core at all
     ("bf16", 1, 8, 2, 3000, 64, 16, 128, cca.CCA_POOL_SOFTMAX),  # d = 64: several core blocks
     ("f32", 1, 4, 1, 1500, 64, 16, 64, cca.CCA_POOL_SOFTMAX),    # d = 64 on the vector ALUs, longer
+    ("bf16", 1, 4, 4, 2500, 128, 16, 256, cca.CCA_POOL_SOFTMAX),  # G = 1 at d = 128 (the MHA layout)
+    ("bf16", 1, 2, 2, 1300, 128, 5, 100, cca.CCA_POOL_MAX),       # G = 1, d = 128, g not a power of 2
 ]
 
 
@@ -122,15 +125,18 @@ def test_backward_is_deterministic_where_no_atomics():
     assert torch.equal(a[0], b[0])
 
 
-def test_backward_full_size():
-    """The 128K GQA workload (B1, 32/8 heads, d128, g16, w1024) at full size, in
-    the launch configuration the benchmark times.  Checked against the oracle
-    for one kv head and its 4 query heads on everything: dq at every row, dk
-    and dv at every position, each with its pooling share.  The oracle runs
-    the masked multi-row form 128 rows at a time, sums the rows'
-    contributions to the raw keys and the cores, then the pooling backward
-    over the whole sequence (about a minute on 16 host cores)."""
-    cfg = cca_inputs.CONFIGS[4]
+@pytest.mark.parametrize("number,kv_heads", [(4, (0,)), (2, (0, 13))], ids=["gqa-128k", "mha-32k"])
+def test_backward_full_size(number, kv_heads):
+    """The 128K GQA workload (B1, 32/8 heads, d128, g16, w1024) and the 32K MHA
+    one (B1, 32/32 heads) at full size, in the launch configuration of the
+    benchmark's backward.  Checked against the oracle for the listed kv heads
+    and their query heads on everything: dq at every row, dk and dv at every
+    position, each with its pooling share (at the MHA workload a second kv
+    head that runs in another slot of its XCD).  The oracle runs the masked
+    multi-row form 128 rows at a time, sums the rows' contributions to the raw
+    keys and the cores, then the pooling backward over the whole sequence
+    (about a minute for the GQA kv head on 16 host cores)."""
+    cfg = cca_inputs.CONFIGS[number]
     B, Hq, Hkv, L, d, g, w = cfg.B, cfg.Hq, cfg.Hkv, cfg.L, cfg.d, cfg.g, cfg.w
     G = Hq // Hkv
     say(f"backward full-size {cfg.name}: generating inputs")
@@ -151,35 +157,38 @@ def test_backward_full_size():
     ws = torch.empty(cca.cca_attn_backward_workspace_bytes(B, Hq, Hkv, L, d, g, q.dtype), dtype=torch.uint8, device=DEV)
     cca.cca_attn_backward(qd, kd, vd, ck, cv, out, lse, gd, dq, dk, dv, ws, g, w)
     torch.cuda.synchronize()
-    hk = 0
-    heads = slice(hk * G, hk * G + G)
-    dq_gpu = dq[:, heads].double().cpu().numpy()
-    dk_gpu = dk[:, hk : hk + 1].double().cpu().numpy()
-    dv_gpu = dv[:, hk : hk + 1].double().cpu().numpy()
+    got = {}
+    for hk in kv_heads:
+        heads = slice(hk * G, hk * G + G)
+        got[hk] = (dq[:, heads].double().cpu().numpy(), dk[:, hk : hk + 1].double().cpu().numpy(),
+                   dv[:, hk : hk + 1].double().cpu().numpy())
     del qd, kd, vd, gd, out, dq, dk, dv, ws
-    say(f"  oracle: kv head {hk}, every row and every key position")
-    Qh, Kh, Vh, Gh = f32np(q[:, heads]), f32np(k[:, hk : hk + 1]), f32np(v[:, hk : hk + 1]), f32np(dO[:, heads])
-    CK, CV, _ = orc.pool_core(Qh, Kh, Vh, g)
-    dq_ref = np.zeros((B, G, L, d))
-    dk_ref, dv_ref = np.zeros((B, 1, L, d)), np.zeros((B, 1, L, d))
-    dCK, dCV = np.zeros((B, 1, m, d)), np.zeros((B, 1, m, d))
-    for t0 in range(0, L, 128):
-        t1 = min(L, t0 + 128)
-        q_, k_, v_, ck_, cv_, lo = bwd.attn_backward_rows_masked(Qh, Kh, Vh, CK, CV, g, w, Gh, t0, t1)
-        dq_ref[:, :, t0:t1] = q_
-        dk_ref[:, :, lo:t1] += k_
-        dv_ref[:, :, lo:t1] += v_
-        dCK[:, :, : ck_.shape[2]] += ck_
-        dCV[:, :, : cv_.shape[2]] += cv_
-        if t1 % 16384 == 0:
-            say(f"    rows up to {t1}")
-    say("  oracle: pooling backward")
-    pQ, pK, pV = bwd.pool_backward(Qh, Kh, Vh, g, dCK, dCV, "softmax")
-    dq_ref += pQ
-    dk_ref += pK
-    dv_ref += pV
-    for name, x, y in (("dq", dq_gpu, dq_ref), ("dk", dk_gpu, dk_ref), ("dv", dv_gpu, dv_ref)):
-        scale = max(1.0, float(np.abs(y).max()))
-        e = float(np.abs(x - y).max()) / scale
-        say(f"  {name} max err / scale {e:.3e} (scale {scale:.2f})")
-        assert e <= TOL["bf16"], name
+    for hk in kv_heads:
+        heads = slice(hk * G, hk * G + G)
+        dq_gpu, dk_gpu, dv_gpu = got[hk]
+        say(f"  oracle: kv head {hk}, every row and every key position")
+        Qh, Kh, Vh, Gh = f32np(q[:, heads]), f32np(k[:, hk : hk + 1]), f32np(v[:, hk : hk + 1]), f32np(dO[:, heads])
+        CK, CV, _ = orc.pool_core(Qh, Kh, Vh, g)
+        dq_ref = np.zeros((B, G, L, d))
+        dk_ref, dv_ref = np.zeros((B, 1, L, d)), np.zeros((B, 1, L, d))
+        dCK, dCV = np.zeros((B, 1, m, d)), np.zeros((B, 1, m, d))
+        for t0 in range(0, L, 128):
+            t1 = min(L, t0 + 128)
+            q_, k_, v_, ck_, cv_, lo = bwd.attn_backward_rows_masked(Qh, Kh, Vh, CK, CV, g, w, Gh, t0, t1)
+            dq_ref[:, :, t0:t1] = q_
+            dk_ref[:, :, lo:t1] += k_
+            dv_ref[:, :, lo:t1] += v_
+            dCK[:, :, : ck_.shape[2]] += ck_
+            dCV[:, :, : cv_.shape[2]] += cv_
+            if t1 % 16384 == 0:
+                say(f"    rows up to {t1}")
+        say("  oracle: pooling backward")
+        pQ, pK, pV = bwd.pool_backward(Qh, Kh, Vh, g, dCK, dCV, "softmax")
+        dq_ref += pQ
+        dk_ref += pK
+        dv_ref += pV
+        for name, x, y in (("dq", dq_gpu, dq_ref), ("dk", dk_gpu, dk_ref), ("dv", dv_gpu, dv_ref)):
+            scale = max(1.0, float(np.abs(y).max()))
+            e = float(np.abs(x - y).max()) / scale
+            say(f"  kv head {hk}: {name} max err / scale {e:.3e} (scale {scale:.2f})")
+            assert e <= TOL["bf16"], (hk, name)
