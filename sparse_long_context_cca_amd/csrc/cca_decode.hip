@@ -29,6 +29,10 @@ namespace cca {
 namespace {
 
 constexpr int kThreads = 256;
+// The max a split writes for a step whose position is invalid: a quiet NaN
+// with a payload of its own, so that the combine tells it from a NaN the data
+// produced (which must reach the output, with pos still advanced).
+constexpr unsigned kInvalidState = 0x7fc00badu;
 constexpr int kBatch = 4;  // keys per lane group per iteration
 
 template <int DT>
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   const long st_base = ((long)b * Hq + h0) * splits + split;  // partial state of head h0
 
   if (!decode_valid(t, g, m_cap)) {
-    if (threadIdx.x < GT) ws_m[st_base + (long)threadIdx.x * splits] = NAN;
+    if (threadIdx.x < GT) ws_m[st_base + (long)threadIdx.x * splits] = __uint_as_float(kInvalidState);
     return;
   }
 
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(
   const long st_base = ((long)b * Hq + h0) * splits + split;  // state of head h0
 
   if (!decode_valid(t, g, m_cap)) {
-    if ((int)threadIdx.x < G) ws_m[st_base + (long)threadIdx.x * splits] = NAN;
+    if ((int)threadIdx.x < G) ws_m[st_base + (long)threadIdx.x * splits] = __uint_as_float(kInvalidState);
     return;
   }
   const long bkl = bk;
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
     float bad = 0.f;
     for (int s = e; s < splits; s += 64) {
       M = fmaxf(M, sm[s]);
-      bad += isnan(sm[s]) ? 1.f : 0.f;
+      bad += __float_as_uint(sm[s]) == kInvalidState ? 1.f : 0.f;
     }
     M = wave_max(M);
     bad = wave_sum(bad);
@@ -597,7 +601,8 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
   const float M = red[0];
   for (int s = e; s < splits; s += D) {
     const float ms = sm[s];
-    sm[s] = (ms == -INFINITY || isnan(ms)) ? 0.f : exp2f(ms - M);  // weight of split s
+    // weight of split s; a NaN max from the data stays NaN and reaches the output
+    sm[s] = (ms == -INFINITY || __float_as_uint(ms) == kInvalidState) ? 0.f : exp2f(ms - M);
   }
   __syncthreads();
   float lsum = 0.f, osum = 0.f;
@@ -607,8 +612,8 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(
     lsum = fmaf(sl[s], f, lsum);
     osum = fmaf(ws_o[(st0 + s) * D + e], f, osum);
   }
-  // an invalid step (every split marked NaN: validity depends on t alone)
-  // writes NaN and leaves pos where it is
+  // an invalid step (every split marked kInvalidState: validity depends on t
+  // alone) writes NaN and leaves pos where it is
   const bool invalid = red[1] != 0.f;
   const float r = invalid ? NAN : osum / lsum;
   EO::store(static_cast<typename EO::T*>(out_), bh * D + e, r);

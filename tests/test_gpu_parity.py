@@ -502,6 +502,29 @@ def test_decode_out_of_capacity_gives_nan_and_no_writes():
     assert bool((rk[0, :, 7] == 0).all()), "position -1 has no ring slot to write"
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_decode_nan_data_at_a_valid_position_reaches_the_output(dt):
+    """A valid step whose query is NaN (every score NaN) is not an invalid
+    step: its output is NaN and its position still advances; the other
+    sequences of the batch are unaffected."""
+    say(f"decode NaN query at a valid position ({dt})")
+    B, Hq, Hkv, d, g, w, R, m_cap = 2, 8, 2, 128, 4, 8, 8, 8
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    mk = lambda *s: torch.zeros(s, dtype=tdt, device=DEV)
+    q_t, k_t, v_t = mk(B, Hq, d) + 0.5, mk(B, Hkv, d) + 0.25, mk(B, Hkv, d) + 1
+    q_t[1] = float("nan")
+    rk, rv = mk(B, Hkv, R, d) + 0.25, mk(B, Hkv, R, d) + 1
+    ck = torch.ones((B, Hkv, m_cap, d), dtype=cca.core_dtype(tdt), device=DEV)
+    cv = torch.ones_like(ck)
+    pos = torch.tensor([10, 10], dtype=torch.int32, device=DEV)
+    ws = torch.empty(cca.cca_decode_workspace_bytes(B, Hq, Hkv, d, m_cap, g, w), dtype=torch.uint8, device=DEV)
+    out = mk(B, Hq, d)
+    cca.cca_attn_decode(q_t, k_t, v_t, rk, rv, ck, cv, pos, out, ws, g, w, advance_pos=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out[0].float()).all() and torch.isnan(out[1].float()).all()
+    assert pos.tolist() == [11, 11], "a valid step advances its position whatever its data"
+
+
 def test_decode_graph_replay_matches_eager():
     """Decode steps captured in a HIP graph: every replay (with eager work and
     synchronisation in between) reproduces the eager outputs bit for bit."""
