@@ -319,7 +319,8 @@ size_t cca_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int m_cap, int 
  *   form; the device-side advance is an addition for replayed loops.)
  *   A sequence with t < 0, t = INT32_MAX or floor((t+1)/g) > m_cap (no core
  *   slot left) gets NaN outputs, no cache writes and keeps its pos (pos lives
- *   on the device, so this cannot be reported as a status).
+ *   on the device, so this cannot be reported as a status).  Validity depends
+ *   on t alone: NaN inputs at a valid t give NaN outputs and still advance pos.
  * Errors: INVALID_ARG, UNSUPPORTED as above; CAPACITY when R < max(w, g) or
  *   the workspace is too small.
  */
