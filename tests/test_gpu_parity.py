@@ -154,6 +154,25 @@ def test_pool_modes_parity(mode, dt, case):
         assert err(wt[:, :, :m], A) <= 1e-5
 
 
+@pytest.mark.parametrize("mode", [cca.CCA_POOL_SOFTMAX_HEADS, cca.CCA_POOL_MEAN, cca.CCA_POOL_MAX],
+                         ids=lambda m: MODES[m])
+def test_pool_modes_full_size(mode):
+    """The pooling variants on the LLaMA-3.1-8B GQA 128K workload at full size:
+    every core of every kv head against the oracle's pooling of the same rule
+    (max pooling bit for bit, the others within half an fp16 ulp)."""
+    cfg = cca_inputs.CONFIGS[4]
+    say(f"pool mode {MODES[mode]} full size {cfg.name}")
+    q, k, v = cca_inputs.prefill_inputs(cfg)
+    ck, cv, _ = gpu_pool(q.to(DEV), k.to(DEV), v.to(DEV), cfg.g, mode=mode)
+    torch.cuda.synchronize()
+    G = cfg.G
+    for hk in range(cfg.Hkv):
+        CK, CV, _ = orc.pool_core(f32np(q[:, hk * G : hk * G + G]), f32np(k[:, hk : hk + 1]),
+                                  f32np(v[:, hk : hk + 1]), cfg.g, MODES[mode])
+        check_cores(cfg.dtype, ck[:, hk : hk + 1], CK, mode)
+        check_cores(cfg.dtype, cv[:, hk : hk + 1], CV, mode)
+
+
 def test_pool_is_deterministic():
     say("pool determinism")
     cfg = cfg_of("det", 1, 8, 2, 4096, 128, 16, 1, "bf16", seed=5)
