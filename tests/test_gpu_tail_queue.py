@@ -205,3 +205,30 @@ def test_backward_two_streams_at_once():
         torch.cuda.synchronize()
         bw_check(a, ref_a, f"stream 1, round {rep}")
         bw_check(b, ref_b, f"stream 2, round {rep}")
+
+
+def test_backward_graph_replay_matches_eager():
+    """A backward call captured in a HIP graph (it clears its core partial sums
+    with a fill kernel, so the clear replays too): every replay, with eager
+    calls and synchronisation in between, writes every gradient row and agrees
+    with the eager call."""
+    say("backward queues: graph replay")
+    c = bw_case(*BW_BIG, seed=85)
+    other = bw_case(*BW_SMALL, seed=86)
+    ref, ref_other = bw_eager(c), bw_eager(other)
+    dq, dk, dv = c["grads"]
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        cca.cca_attn_backward(c["q"], c["k"], c["v"], c["ck"], c["cv"], c["out"], c["lse"], c["dout"],
+                              dq, dk, dv, c["ws"], c["g"], c["w"], stream=torch.cuda.current_stream())
+    for rep in range(3):
+        for t in c["grads"]:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        bw_check(c, ref, f"replay {rep}")
+        bw_run(other)
+        torch.cuda.synchronize()
+        bw_check(other, ref_other, f"eager call after replay {rep}")
