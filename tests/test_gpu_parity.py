@@ -241,7 +241,9 @@ def test_prefill_parity(kernel, dt, out_dt, case):
     assert e <= TOL[dt]
 
 
-def test_prefill_c1_tiny_config():
+def test_prefill_tiny_f32_L1024():
+    """The fp32 workload: L=1024, one head, d=64, g=16, w=64, on the vector-ALU
+    kernel, against the oracle within 1e-4."""
     cfg = cca_inputs.CONFIGS[1]
     say(f"prefill config {cfg.name}")
     (q, k, v), out = run_prefill(cfg, 0, "f32")
@@ -668,7 +670,7 @@ def test_decode_two_streams_match_sequential():
             assert L["pos"].tolist() == [p + steps for p in pos0]
 
 
-def test_decode_c5_config():
+def test_decode_batch8_ctx65536_all_steps():
     """The decode workload: batch 8, 32/8 heads, 65536 cached tokens (cores from
     the pool kernel, raw ring of 1024), 256 steps; every step, every (b, h)."""
     cfg = cca_inputs.CONFIGS[5]
